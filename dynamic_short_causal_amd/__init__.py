@@ -1,0 +1,186 @@
+"""Python binding of ``libdsc.so``, the gfx950 dynamic short causal convolution.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/dsc.h``.  PyTorch supplies device memory
+and the current stream.  There is no CPU or PyTorch fallback: if the library
+is missing, importing this package raises.
+
+The functions named like the C entry points (``dsc_headwise_fwd`` ...) take
+pre-allocated output tensors; ``headwise_fwd`` and friends allocate them with
+``torch.empty`` and call the former.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsc.so")
+
+DSC_OK, DSC_ERR_INVALID_ARG, DSC_ERR_UNSUPPORTED, DSC_ERR_WORKSPACE, DSC_ERR_HIP = range(5)
+DSC_F32, DSC_BF16 = 0, 1
+DSC_RESIDUAL, DSC_ACT_SILU = 1, 2
+
+# every symbol declared in include/dsc.h
+EXPORTS = ("dsc_version", "dsc_status_string", "dsc_last_error", "dsc_headwise_fwd",
+           "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd_workspace_bytes",
+           "dsc_lowrank_bwd")
+
+
+class DscError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with dynamic_short_causal_amd/build.py "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, ci, cu = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
+    lib.dsc_version.restype = ci
+    lib.dsc_status_string.restype = ctypes.c_char_p
+    lib.dsc_status_string.argtypes = [ci]
+    lib.dsc_last_error.restype = ctypes.c_char_p
+    lib.dsc_headwise_fwd.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, cu, vp]
+    lib.dsc_headwise_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, cu, vp]
+    lib.dsc_lowrank_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, ci, cu, vp]
+    lib.dsc_lowrank_bwd_workspace_bytes.argtypes = [i64, i64, i64, ci, ci, ci, ci]
+    lib.dsc_lowrank_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.dsc_lowrank_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
+                                    i64, ci, ci, ci, ci, cu, vp]
+    for name in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd",
+                 "dsc_lowrank_bwd"):
+        getattr(lib, name).restype = ci
+    return lib
+
+
+LIB = _load()
+
+
+def _status_name(s):
+    return LIB.dsc_status_string(int(s)).decode()
+
+
+def version():
+    return int(LIB.dsc_version())
+
+
+def _check(status):
+    if status != DSC_OK:
+        raise DscError(status, LIB.dsc_last_error().decode())
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return DSC_BF16
+    if t.dtype == torch.float32:
+        return DSC_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _flags(residual, act):
+    return (DSC_RESIDUAL if residual else 0) | (DSC_ACT_SILU if act else 0)
+
+
+def _need(t, name, shape, dtype):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+# --------------------------------------------------------------- C-named calls
+def dsc_headwise_fwd(x, w, y, H, residual=False, act=False, stream=None):
+    B, T, D = x.shape
+    W = w.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("w", w, (B, T, D // H, W)), ("y", y, (B, T, D))):
+        _need(t, n, s, x.dtype)
+    _check(LIB.dsc_headwise_fwd(_ptr(x), _ptr(w), _ptr(y), B, T, D, W, H, _dtype(x),
+                                _flags(residual, act), _stream(stream)))
+    return y
+
+
+def dsc_headwise_bwd(x, w, dy, dx, dw, H, residual=False, act=False, stream=None):
+    B, T, D = x.shape
+    W = w.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("w", w, (B, T, D // H, W)), ("dy", dy, (B, T, D)),
+                    ("dx", dx, (B, T, D)), ("dw", dw, (B, T, D // H, W))):
+        _need(t, n, s, x.dtype)
+    _check(LIB.dsc_headwise_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(dx), _ptr(dw), B, T, D, W, H,
+                                _dtype(x), _flags(residual, act), _stream(stream)))
+    return dx, dw
+
+
+def dsc_lowrank_fwd(x, z, U, y, W, H, residual=False, act=False, stream=None):
+    B, T, D = x.shape
+    R = z.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("z", z, (B, T, R)), ("U", U, (R, (D // H) * W)),
+                    ("y", y, (B, T, D))):
+        _need(t, n, s, x.dtype)
+    _check(LIB.dsc_lowrank_fwd(_ptr(x), _ptr(z), _ptr(U), _ptr(y), B, T, D, W, H, R,
+                               _dtype(x), _flags(residual, act), _stream(stream)))
+    return y
+
+
+def dsc_lowrank_bwd_workspace_bytes(B, T, D, W, H, R, dtype):
+    d = DSC_BF16 if dtype == torch.bfloat16 else DSC_F32
+    return int(LIB.dsc_lowrank_bwd_workspace_bytes(B, T, D, W, H, R, d))
+
+
+def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace, W, H, residual=False, act=False,
+                    stream=None):
+    B, T, D = x.shape
+    R = z.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("z", z, (B, T, R)), ("U", U, (R, (D // H) * W)),
+                    ("dy", dy, (B, T, D)), ("dx", dx, (B, T, D)), ("dz", dz, (B, T, R)),
+                    ("dU", dU, (R, (D // H) * W))):
+        _need(t, n, s, x.dtype)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.dsc_lowrank_bwd(_ptr(x), _ptr(z), _ptr(U), _ptr(dy), _ptr(dx), _ptr(dz),
+                               _ptr(dU), _ptr(workspace), nbytes, B, T, D, W, H, R,
+                               _dtype(x), _flags(residual, act), _stream(stream)))
+    return dx, dz, dU
+
+
+# --------------------------------------------------------------- allocating forms
+def headwise_fwd(x, w, H, residual=False, act=False, stream=None):
+    return dsc_headwise_fwd(x, w, torch.empty_like(x), H, residual, act, stream)
+
+
+def headwise_bwd(x, w, dy, H, residual=False, act=False, stream=None):
+    return dsc_headwise_bwd(x, w, dy, torch.empty_like(x), torch.empty_like(w), H, residual,
+                            act, stream)
+
+
+def lowrank_fwd(x, z, U, W, H, residual=False, act=False, stream=None):
+    return dsc_lowrank_fwd(x, z, U, torch.empty_like(x), W, H, residual, act, stream)
+
+
+def lowrank_workspace(x, z, W, H):
+    B, T, D = x.shape
+    n = dsc_lowrank_bwd_workspace_bytes(B, T, D, W, H, z.shape[-1], x.dtype)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+
+
+def lowrank_bwd(x, z, U, dy, W, H, residual=False, act=False, workspace=None, stream=None):
+    if workspace is None:
+        workspace = lowrank_workspace(x, z, W, H)
+    return dsc_lowrank_bwd(x, z, U, dy, torch.empty_like(x), torch.empty_like(z),
+                           torch.empty_like(U), workspace, W, H, residual, act, stream)

@@ -1,0 +1,240 @@
+// dsc_abi.cpp -- the C ABI declared in include/dsc.h: host-side argument
+// checks, then dispatch to the gfx950 kernel launchers.  No allocation, no
+// synchronisation, no state kept between calls.
+#include "../../include/dsc.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "dsc_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsc_status fail(dsc_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dsc_status ok() {
+  g_err[0] = '\0';
+  return DSC_OK;
+}
+
+struct Span {
+  const char *name;
+  uintptr_t lo, hi;  // [lo, hi) bytes; empty when lo == hi
+  bool output;
+};
+
+bool overlap(const Span &a, const Span &b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+const int64_t kMaxElems = (int64_t)1 << 62;
+
+// Common shape / dtype / flag checks.  On success sets *V.
+dsc_status check_common(int64_t B, int64_t T, int64_t D, int W, int H, dsc_dtype dtype,
+                        unsigned flags, int *V) {
+  if (dtype != DSC_F32 && dtype != DSC_BF16)
+    return fail(DSC_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (flags & ~(DSC_RESIDUAL | DSC_ACT_SILU))
+    return fail(DSC_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if (B < 0 || T < 0) return fail(DSC_ERR_INVALID_ARG, "B=%lld and T=%lld must be >= 0",
+                                  (long long)B, (long long)T);
+  if (D < 1) return fail(DSC_ERR_INVALID_ARG, "D=%lld must be >= 1", (long long)D);
+  if (B > INT32_MAX || T > INT32_MAX || D > INT32_MAX)
+    return fail(DSC_ERR_INVALID_ARG, "B, T and D must each be below 2^31");
+  if (B > 0 && T > 0 && (B * T > kMaxElems / D))
+    return fail(DSC_ERR_INVALID_ARG, "B*T*D exceeds 2^62 elements");
+  if (W < 1 || W > 8) return fail(DSC_ERR_UNSUPPORTED, "W=%d outside 1..8", W);
+  if (H < 1) return fail(DSC_ERR_INVALID_ARG, "H=%d must be >= 1", H);
+  if (D % H) return fail(DSC_ERR_INVALID_ARG, "D=%lld is not a multiple of H=%d",
+                         (long long)D, H);
+  *V = dtype == DSC_BF16 ? 8 : 4;
+  if (D % *V)
+    return fail(DSC_ERR_INVALID_ARG, "D=%lld is not a multiple of the %d-element vector",
+                (long long)D, *V);
+  return DSC_OK;
+}
+
+dsc_status check_ptrs(const Span *s, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (s[i].lo == s[i].hi) continue;  // empty tensor: pointer not used
+    if (s[i].lo == 0) return fail(DSC_ERR_INVALID_ARG, "%s is NULL", s[i].name);
+    if (s[i].lo % 16) return fail(DSC_ERR_INVALID_ARG, "%s is not 16-byte aligned", s[i].name);
+  }
+  for (int i = 0; i < n; ++i) {
+    if (!s[i].output) continue;
+    for (int j = 0; j < n; ++j) {
+      if (j == i || (s[j].output && j < i)) continue;
+      if (overlap(s[i], s[j]))
+        return fail(DSC_ERR_INVALID_ARG, "output %s overlaps %s", s[i].name, s[j].name);
+    }
+  }
+  return DSC_OK;
+}
+
+Span span(const char *name, const void *p, int64_t elems, int esize, bool out) {
+  uintptr_t lo = (uintptr_t)p;
+  return Span{name, lo, lo + (uintptr_t)(elems * esize), out};
+}
+
+bool headwise_h_ok(int H, int V) {
+  if (V % H == 0) return true;
+  if (H % V) return false;
+  int L = H / V;
+  return L <= 64 && (L & (L - 1)) == 0;
+}
+
+dsc_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  return fail(DSC_ERR_HIP, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsc_version(void) { return 10000; }
+
+const char *dsc_status_string(dsc_status s) {
+  switch (s) {
+    case DSC_OK: return "DSC_OK";
+    case DSC_ERR_INVALID_ARG: return "DSC_ERR_INVALID_ARG";
+    case DSC_ERR_UNSUPPORTED: return "DSC_ERR_UNSUPPORTED";
+    case DSC_ERR_WORKSPACE: return "DSC_ERR_WORKSPACE";
+    case DSC_ERR_HIP: return "DSC_ERR_HIP";
+  }
+  return "DSC_ERR_UNKNOWN";
+}
+
+const char *dsc_last_error(void) { return g_err; }
+
+static dsc_status headwise_common(const void *x, const void *w, const void *dy, void *y,
+                                  void *dx, void *dw, int64_t B, int64_t T, int64_t D, int W,
+                                  int H, dsc_dtype dtype, unsigned flags, void *stream,
+                                  bool bwd) {
+  int V = 0;
+  dsc_status st = check_common(B, T, D, W, H, dtype, flags, &V);
+  if (st != DSC_OK) return st;
+  if (!headwise_h_ok(H, V))
+    return fail(DSC_ERR_UNSUPPORTED,
+                "H=%d: head-wise needs H | %d or H = %d * 2^m with 2^m <= 64", H, V, V);
+  const int es = dtype == DSC_BF16 ? 2 : 4;
+  const int64_t n_act = B * T * D, n_w = B * T * (D / H) * W;
+  if (!bwd) {
+    Span s[3] = {span("x", x, n_act, es, false), span("w", w, n_w, es, false),
+                 span("y", y, n_act, es, true)};
+    if ((st = check_ptrs(s, 3)) != DSC_OK) return st;
+  } else {
+    Span s[5] = {span("x", x, n_act, es, false), span("w", w, n_w, es, false),
+                 span("dy", dy, n_act, es, false), span("dx", dx, n_act, es, true),
+                 span("dw", dw, n_w, es, true)};
+    if ((st = check_ptrs(s, 5)) != DSC_OK) return st;
+  }
+  dsc::HwArgs a{};
+  a.x = x; a.w = w; a.dy = dy; a.y = y; a.dx = dx; a.dw = dw;
+  a.B = B; a.T = T; a.D = D; a.W = W; a.H = H;
+  a.bf16 = dtype == DSC_BF16;
+  a.residual = (flags & DSC_RESIDUAL) != 0;
+  a.act = (flags & DSC_ACT_SILU) != 0;
+  a.bwd = bwd;
+  a.stream = stream;
+  return hip_status(dsc::headwise_launch(a));
+}
+
+dsc_status dsc_headwise_fwd(const void *x, const void *w, void *y, int64_t B, int64_t T,
+                            int64_t D, int W, int H, dsc_dtype dtype, unsigned flags,
+                            void *stream) {
+  return headwise_common(x, w, nullptr, y, nullptr, nullptr, B, T, D, W, H, dtype, flags,
+                         stream, false);
+}
+
+dsc_status dsc_headwise_bwd(const void *x, const void *w, const void *dy, void *dx, void *dw,
+                            int64_t B, int64_t T, int64_t D, int W, int H, dsc_dtype dtype,
+                            unsigned flags, void *stream) {
+  return headwise_common(x, w, dy, nullptr, dx, dw, B, T, D, W, H, dtype, flags, stream,
+                         true);
+}
+
+static dsc_status lowrank_check(int64_t B, int64_t T, int64_t D, int W, int H, int R,
+                                dsc_dtype dtype, unsigned flags, int *V) {
+  dsc_status st = check_common(B, T, D, W, H, dtype, flags, V);
+  if (st != DSC_OK) return st;
+  if (*V % H)
+    return fail(DSC_ERR_UNSUPPORTED, "H=%d: low-rank needs H to divide %d", H, *V);
+  if (R < 1 || R > 64) return fail(DSC_ERR_UNSUPPORTED, "R=%d outside 1..64", R);
+  return DSC_OK;
+}
+
+dsc_status dsc_lowrank_fwd(const void *x, const void *z, const void *U, void *y, int64_t B,
+                           int64_t T, int64_t D, int W, int H, int R, dsc_dtype dtype,
+                           unsigned flags, void *stream) {
+  int V = 0;
+  dsc_status st = lowrank_check(B, T, D, W, H, R, dtype, flags, &V);
+  if (st != DSC_OK) return st;
+  const int es = dtype == DSC_BF16 ? 2 : 4;
+  const int64_t n_act = B * T * D;
+  Span s[4] = {span("x", x, n_act, es, false), span("z", z, B * T * R, es, false),
+               span("U", U, (int64_t)R * (D / H) * W, es, false),
+               span("y", y, n_act, es, true)};
+  if ((st = check_ptrs(s, 4)) != DSC_OK) return st;
+  dsc::LrArgs a{};
+  a.x = x; a.z = z; a.U = U; a.y = y;
+  a.B = B; a.T = T; a.D = D; a.W = W; a.H = H; a.R = R;
+  a.bf16 = dtype == DSC_BF16;
+  a.residual = (flags & DSC_RESIDUAL) != 0;
+  a.act = (flags & DSC_ACT_SILU) != 0;
+  a.bwd = false;
+  a.stream = stream;
+  return hip_status(dsc::lowrank_launch(a));
+}
+
+size_t dsc_lowrank_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int W, int H, int R,
+                                       dsc_dtype dtype) {
+  int V = 0;
+  if (lowrank_check(B, T, D, W, H, R, dtype, 0, &V) != DSC_OK) return 0;
+  return dsc::lr_bwd_plan(B, T, D, W, H, R, dtype == DSC_BF16).bytes;
+}
+
+dsc_status dsc_lowrank_bwd(const void *x, const void *z, const void *U, const void *dy,
+                           void *dx, void *dz, void *dU, void *workspace,
+                           size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int W,
+                           int H, int R, dsc_dtype dtype, unsigned flags, void *stream) {
+  int V = 0;
+  dsc_status st = lowrank_check(B, T, D, W, H, R, dtype, flags, &V);
+  if (st != DSC_OK) return st;
+  const int es = dtype == DSC_BF16 ? 2 : 4;
+  const int64_t n_act = B * T * D, n_z = B * T * R, n_U = (int64_t)R * (D / H) * W;
+  const dsc::LrBwdPlan p = dsc::lr_bwd_plan(B, T, D, W, H, R, dtype == DSC_BF16);
+  Span s[8] = {span("x", x, n_act, es, false),   span("z", z, n_z, es, false),
+               span("U", U, n_U, es, false),     span("dy", dy, n_act, es, false),
+               span("dx", dx, n_act, es, true),  span("dz", dz, n_z, es, true),
+               span("dU", dU, n_U, es, true),
+               span("workspace", workspace, (int64_t)p.bytes, 1, true)};
+  if (p.bytes > 0 && workspace_bytes < p.bytes)
+    return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed",
+                workspace_bytes, p.bytes);
+  if (p.bytes > 0 && workspace == nullptr)
+    return fail(DSC_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", p.bytes);
+  if ((st = check_ptrs(s, 8)) != DSC_OK) return st;
+  dsc::LrArgs a{};
+  a.x = x; a.z = z; a.U = U; a.dy = dy; a.dx = dx; a.dz = dz; a.dU = dU; a.ws = workspace;
+  a.B = B; a.T = T; a.D = D; a.W = W; a.H = H; a.R = R;
+  a.bf16 = dtype == DSC_BF16;
+  a.residual = (flags & DSC_RESIDUAL) != 0;
+  a.act = (flags & DSC_ACT_SILU) != 0;
+  a.bwd = true;
+  a.stream = stream;
+  return hip_status(dsc::lowrank_launch(a));
+}
+
+}  // extern "C"

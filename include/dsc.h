@@ -1,0 +1,144 @@
+/*
+ * dsc.h -- C ABI of the MI355X (gfx950) dynamic short causal convolution.
+ *
+ * The operation ([gist] = gist.science technical summary "Dynamische Korte
+ * Convoluties Verbeteren Transformers", section Methodologie > Dynamische
+ * Korte Convoluties):
+ *
+ *   s[b,t,c] = sum_{k=0}^{W-1} w[b,t,g(c),k] * x[b,t-k,c]     (bullet Mechanisme)
+ *   y[b,t,c] = act(s[b,t,c]) + rho * x[b,t,c]                 (bullet Plaatsing:
+ *                                                              X + conv(X))
+ *
+ * with g(c) = floor(c / H): one filter shared by H consecutive channels
+ * (bullet Parametrisatie, 2. head-wise tying), G = D / H groups.  In the
+ * low-rank form (Parametrisatie, 1.; section Efficiente
+ * Trainingsimplementatie, bullet Fused Low-Rank Kernel) the filters are the
+ * product w[b,t,g,k] = sum_r z[b,t,r] * U[r, g*W + k], generated on chip and
+ * never written to device memory.  Taps before the start of a sequence read
+ * zero; sequences b are independent.  rho is 1 with DSC_RESIDUAL, else 0;
+ * act is SiLU, s * sigmoid(s), with DSC_ACT_SILU, else the identity.
+ *
+ * Layouts: every tensor is dense, row-major, in device memory:
+ *   x, y, dy, dx : (B, T, D)         w, dw : (B, T, G, W)   (tap k = 0 is x_t)
+ *   z, dz        : (B, T, R)         U, dU : (R, G*W)       (column g*W + k)
+ * All tensors of one call share its dtype (DSC_F32 or DSC_BF16).  Arithmetic
+ * is fp32; bf16 results are rounded to nearest even once, at the store.  In
+ * the low-rank path the products z*U are formed from the bf16 (or fp32)
+ * inputs and summed in fp32.
+ *
+ * Ownership and execution: the caller owns every buffer (workspace
+ * included).  The library never allocates, frees or synchronises, keeps no
+ * pointer after a call returns and holds no state between calls.  Work is
+ * queued on `stream` (a hipStream_t; NULL is the legacy default stream) and
+ * runs asynchronously; faults during execution surface at the caller's next
+ * synchronisation, as usual in HIP.  Outputs are overwritten, never
+ * accumulated into.  Results are bitwise reproducible for a given shape,
+ * dtype and flags: no atomics, and every cross-tile sum runs in a fixed order.
+ *
+ * Argument checks run on the host before anything is queued.  A failing call
+ * returns an error, queues nothing and changes nothing; dsc_last_error()
+ * then names the failing check.  Errors:
+ *   DSC_ERR_INVALID_ARG  a size < 0 or D < 1, D % H != 0, D not a multiple of
+ *                        the vector width (8 for bf16, 4 for fp32), a NULL
+ *                        pointer for a non-empty tensor, a pointer not 16-byte
+ *                        aligned, an output overlapping another tensor of the
+ *                        call, or an element count above 2^62;
+ *   DSC_ERR_UNSUPPORTED  W outside 1..8, R outside 1..64, an unknown flag or
+ *                        dtype, or a tying factor H the kernels do not tile
+ *                        (head-wise: H divides the vector width, or H is the
+ *                        vector width times a power of two up to 64; low-rank:
+ *                        H divides the vector width);
+ *   DSC_ERR_WORKSPACE    workspace smaller than dsc_lowrank_bwd_workspace_bytes
+ *                        (or NULL while that is non-zero);
+ *   DSC_ERR_HIP          a HIP launch error (the message holds HIP's text).
+ * B == 0 or T == 0 is legal and empty; the low-rank backward then still
+ * writes dU = 0.
+ */
+#ifndef DSC_H_
+#define DSC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsc_status {
+  DSC_OK = 0,
+  DSC_ERR_INVALID_ARG = 1,
+  DSC_ERR_UNSUPPORTED = 2,
+  DSC_ERR_WORKSPACE = 3,
+  DSC_ERR_HIP = 4
+} dsc_status;
+
+typedef enum dsc_dtype { DSC_F32 = 0, DSC_BF16 = 1 } dsc_dtype;
+
+#define DSC_RESIDUAL 1u /* y = act(s) + x ; dx gains + dy */
+#define DSC_ACT_SILU 2u /* act = SiLU on the convolution output */
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dsc_version(void);
+
+/* Static text of a status code. */
+const char *dsc_status_string(dsc_status status);
+
+/* Detail of the last failing call made on this thread ("" if none). */
+const char *dsc_last_error(void);
+
+/*
+ * Head-wise forward: y from x (B,T,D) and per-token filters w (B,T,G,W).
+ * Reads x and w once each and writes y once; the whole window sum happens on
+ * chip ([gist] Efficiente Trainingsimplementatie, bullet On-chip Computatie).
+ */
+dsc_status dsc_headwise_fwd(const void *x, const void *w, void *y, int64_t B,
+                            int64_t T, int64_t D, int W, int H, dsc_dtype dtype,
+                            unsigned flags, void *stream);
+
+/*
+ * Head-wise backward: given dy = dL/dy, writes
+ *   dx[b,tau,c] = sum_{k<W, tau+k<T} w[b,tau+k,g(c),k] * ds[b,tau+k,c] + rho*dy[b,tau,c]
+ *   dw[b,t,g,k] = sum_{c : g(c)=g} ds[b,t,c] * x[b,t-k,c]     (0 when t-k < 0)
+ * with ds = dy * act'(s) (s recomputed on chip when act is SiLU, else ds = dy).
+ * The derivative of the forward above; the pages give the forward only.
+ */
+dsc_status dsc_headwise_bwd(const void *x, const void *w, const void *dy,
+                            void *dx, void *dw, int64_t B, int64_t T, int64_t D,
+                            int W, int H, dsc_dtype dtype, unsigned flags,
+                            void *stream);
+
+/*
+ * Low-rank forward: y from x (B,T,D), z (B,T,R) and U (R, G*W).  Filters
+ * w = zU are formed on chip per token tile and consumed at once; they never
+ * reach device memory ([gist] bullet Fused Low-Rank Kernel).
+ */
+dsc_status dsc_lowrank_fwd(const void *x, const void *z, const void *U, void *y,
+                           int64_t B, int64_t T, int64_t D, int W, int H, int R,
+                           dsc_dtype dtype, unsigned flags, void *stream);
+
+/* Bytes of device workspace dsc_lowrank_bwd needs for this shape (fp32 partial
+ * sums of dz over channel blocks and of dU over token chunks).  Returns 0 for
+ * arguments dsc_lowrank_bwd would reject. */
+size_t dsc_lowrank_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int W,
+                                       int H, int R, dsc_dtype dtype);
+
+/*
+ * Low-rank backward: with w = zU and dw as in dsc_headwise_bwd (formed on chip
+ * only), writes dx (B,T,D) and
+ *   dz[b,t,r]    = sum_{g,k} dw[b,t,g,k] * U[r, g*W+k]
+ *   dU[r, g*W+k] = sum_{b,t} z[b,t,r] * dw[b,t,g,k]
+ * Partial sums go to `workspace` (at least dsc_lowrank_bwd_workspace_bytes);
+ * a second kernel on the same stream adds them in a fixed order.  The
+ * workspace content on entry is ignored and on exit is unspecified.
+ */
+dsc_status dsc_lowrank_bwd(const void *x, const void *z, const void *U,
+                           const void *dy, void *dx, void *dz, void *dU,
+                           void *workspace, size_t workspace_bytes, int64_t B,
+                           int64_t T, int64_t D, int W, int H, int R,
+                           dsc_dtype dtype, unsigned flags, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSC_H_ */

@@ -1,0 +1,130 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before anything is queued.
+
+No call here reaches a kernel launch: every case fails a host-side check (or
+is empty, which queues nothing), so these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsc.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from dynamic_short_causal_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    import dynamic_short_causal_amd as d
+    return d.LIB
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    import dynamic_short_causal_amd as d
+    names = declared()
+    assert names and set(names) == set(d.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.dsc_status_string(0) == b"DSC_OK"
+    assert lib.dsc_status_string(3) == b"DSC_ERR_WORKSPACE"
+    assert lib.dsc_version() >= 10000
+
+
+A = 1 << 20          # fake, 16-byte aligned, never dereferenced
+BIG = 1 << 40
+
+
+def hw(lib, x=A, w=A + BIG, y=A + 2 * BIG, B=1, T=8, D=64, W=4, H=1, dt=1, fl=0):
+    return lib.dsc_headwise_fwd(ctypes.c_void_p(x), ctypes.c_void_p(w), ctypes.c_void_p(y),
+                                B, T, D, W, H, dt, fl, None)
+
+
+def hwb(lib, x=A, w=A + BIG, dy=A + 2 * BIG, dx=A + 3 * BIG, dw=A + 4 * BIG, B=1, T=8, D=64,
+        W=4, H=1, dt=1, fl=0):
+    p = ctypes.c_void_p
+    return lib.dsc_headwise_bwd(p(x), p(w), p(dy), p(dx), p(dw), B, T, D, W, H, dt, fl, None)
+
+
+def lr(lib, x=A, z=A + BIG, U=A + 2 * BIG, y=A + 3 * BIG, B=1, T=8, D=64, W=4, H=1, R=16,
+       dt=1, fl=0):
+    p = ctypes.c_void_p
+    return lib.dsc_lowrank_fwd(p(x), p(z), p(U), p(y), B, T, D, W, H, R, dt, fl, None)
+
+
+def lrb(lib, ws=A + 7 * BIG, wsb=None, B=1, T=8, D=64, W=4, H=1, R=16, dt=1, fl=0, dx=None):
+    p = ctypes.c_void_p
+    if wsb is None:
+        wsb = lib.dsc_lowrank_bwd_workspace_bytes(B, T, D, W, H, R, dt)
+    return lib.dsc_lowrank_bwd(p(A), p(A + BIG), p(A + 2 * BIG), p(A + 3 * BIG),
+                               p(dx if dx is not None else A + 4 * BIG), p(A + 5 * BIG),
+                               p(A + 6 * BIG), p(ws), wsb, B, T, D, W, H, R, dt, fl, None)
+
+
+INVALID, UNSUP, WS = 1, 2, 3
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), UNSUP), (dict(fl=4), UNSUP), (dict(B=-1), INVALID), (dict(T=-2), INVALID),
+    (dict(D=0), INVALID), (dict(W=0), UNSUP), (dict(W=9), UNSUP), (dict(H=0), INVALID),
+    (dict(D=60, H=7), INVALID), (dict(D=36, H=1), INVALID), (dict(D=36, H=1, dt=0), OK := 0),
+    (dict(H=3, D=48), UNSUP), (dict(H=24, D=48), UNSUP), (dict(H=8 * 128, D=8192), UNSUP),
+    (dict(x=0), INVALID), (dict(y=0), INVALID), (dict(w=A + BIG + 2), INVALID),
+    (dict(y=A + 8), INVALID), (dict(y=A + 64 * 8 * 2 - 16), INVALID),
+    (dict(B=1 << 31), INVALID),
+])
+def test_headwise_fwd_checks(lib, kw, code):
+    if code == 0:
+        pytest.skip("valid arguments would launch a kernel")
+    assert hw(lib, **kw) == code, lib.dsc_last_error()
+    assert lib.dsc_last_error() != b""
+
+
+def test_headwise_bwd_overlaps(lib):
+    assert hwb(lib, dx=A + 2 * BIG + 16) == INVALID          # dx overlaps dy
+    assert hwb(lib, dw=A + 3 * BIG + 32) == INVALID          # dw overlaps dx
+    assert hwb(lib, dw=A + 16) == INVALID                    # dw overlaps x
+    assert b"overlaps" in lib.dsc_last_error()
+    assert hwb(lib, dy=0) == INVALID
+    assert hwb(lib, H=5, D=40) == UNSUP
+
+
+def test_empty_is_ok_and_queues_nothing(lib):
+    assert hw(lib, B=0, x=0, w=0, y=0) == 0
+    assert hw(lib, T=0, x=0, w=0, y=0) == 0
+    assert hwb(lib, B=0, x=0, w=0, dy=0, dx=0, dw=0) == 0
+    assert lr(lib, T=0, x=0, z=0, y=0) == 0
+
+
+def test_lowrank_checks(lib):
+    assert lr(lib, H=16, D=64) == UNSUP
+    assert lr(lib, R=0) == UNSUP
+    assert lr(lib, R=65) == UNSUP
+    assert lr(lib, U=0) == INVALID
+    assert lr(lib, y=A + BIG + 8) == INVALID                 # y overlaps z
+    assert lr(lib, H=3, D=48, dt=0) == UNSUP
+    assert lr(lib, H=2, D=48, dt=0, x=A + 4) == INVALID
+
+
+def test_workspace_checks(lib):
+    n = lib.dsc_lowrank_bwd_workspace_bytes(8, 2048, 6144, 4, 1, 16, 1)
+    assert n > 0
+    assert lib.dsc_lowrank_bwd_workspace_bytes(8, 2048, 6144, 4, 16, 16, 1) == 0  # H=16
+    assert lib.dsc_lowrank_bwd_workspace_bytes(8, 2048, 6144, 9, 1, 16, 1) == 0
+    assert lrb(lib, wsb=lib.dsc_lowrank_bwd_workspace_bytes(1, 8, 64, 4, 1, 16, 1) - 1) == WS
+    assert lrb(lib, ws=0) == WS
+    assert lrb(lib, ws=A + 4 * BIG + 16) == INVALID          # workspace overlaps dx
+    assert lrb(lib, R=70) == UNSUP
+    assert lrb(lib, dx=A + 8) == INVALID
