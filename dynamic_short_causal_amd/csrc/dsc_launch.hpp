@@ -36,7 +36,7 @@ struct LrBwdPlan {
   int64_t ncb;      // channel blocks
   int tc;           // tokens per workgroup chunk (multiple of 16)
   int64_t nchunk;   // chunks per sequence
-  int64_t rpad;     // R rounded up to a multiple of 16
+  int64_t rpad;     // R padded to one 16-row MFMA block
   size_t dz_part;   // bytes of dz partials: ncb * B*T * rpad * 4
   size_t dU_part;   // bytes of dU partials: B*nchunk * rpad * G*W * 4
   size_t bytes;     // total workspace
@@ -47,10 +47,11 @@ inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int 
   LrBwdPlan p{};
   p.V = bf16 ? 8 : 4;
   p.gpv = p.V / H;
-  p.units = p.V / p.gpv;  // == H: keeps the slots per lane at V * W
+  const int numax = W <= 5 ? 4 : W <= 7 ? 2 : 1;  // must match LrGeo::NU
+  p.units = H < numax ? H : numax;   // channel vectors per lane
   p.cb = (int64_t)4 /*waves*/ * 4 /*quarters*/ * p.units * p.V;
   p.ncb = (D + p.cb - 1) / p.cb;
-  p.rpad = (R + 15) / 16 * 16;
+  p.rpad = 16;  // R <= 16: one 16-row MFMA block of ranks
   // Long chunks keep the dU partials small; enough workgroups to fill the
   // chip (>= 2 per CU) bound the length from above.
   int tc = 1024;

@@ -1,0 +1,93 @@
+// ---------------------------------------------------------------------------
+// Host-side launchers, instantiated per dtype and direction in
+// lowrank_{fwd,bwd}_{bf16,f32}.hip so the four parts compile in parallel.
+// ---------------------------------------------------------------------------
+#pragma once
+#include "lowrank_impl.hpp"
+
+namespace dsc {
+
+template <typename E, int W, int GPV, bool ACT, int RB>
+static hipError_t launch_lr_fwd(const LrArgs &a) {
+  using Gm = LrGeo<E, W, GPV>;
+  hipStream_t s = (hipStream_t)a.stream;
+  const float rho = a.residual ? 1.f : 0.f;
+  const int TC = a.T >= 256 ? 256 : (int)((a.T + 15) / 16 * 16);
+  const int nchunk = (int)((a.T + TC - 1) / TC);
+  const int ncb = (int)((a.D + Gm::CB - 1) / Gm::CB);
+  const int64_t nblocks = a.B * nchunk * (int64_t)ncb;
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((lr_fwd_kernel<E, W, GPV, ACT, RB>), dim3((unsigned)nblocks),
+                     dim3(kLrThreads), 0, s, (const E *)a.x, (const E *)a.z, (const E *)a.U,
+                     (E *)a.y, (int)a.T, (int)a.D, a.R, TC, nchunk, ncb, rho);
+  return hipGetLastError();
+}
+
+template <typename E, int W, int GPV, int RB>
+static hipError_t launch_lr_bwd(const LrArgs &a) {
+  hipStream_t s = (hipStream_t)a.stream;
+  const float rho = a.residual ? 1.f : 0.f;
+  const int64_t GW = (a.D / a.H) * a.W;
+  const LrBwdPlan p = lr_bwd_plan(a.B, a.T, a.D, a.W, a.H, a.R, a.bf16);
+  const int64_t N = a.B * a.T;
+  float *dzp = (float *)a.ws;
+  float *dUp = (float *)((char *)a.ws + p.dz_part);
+  const int64_t nblocks = a.B * p.nchunk * p.ncb;
+  if (nblocks > 0) {
+    using Sm = LrBwdSmem<E, W, GPV, RB>;
+    hipLaunchKernelGGL((lr_bwd_kernel<E, W, GPV, RB>), dim3((unsigned)nblocks),
+                       dim3(kLrThreads), Sm::bytes, s, (const E *)a.x, (const E *)a.z,
+                       (const E *)a.U, (const E *)a.dy, (E *)a.dx, dzp, dUp, (int)a.T, (int)a.D,
+                       a.R, p.tc, (int)p.nchunk, (int)p.ncb, N, rho, a.act ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t total = N * a.R + (int64_t)a.R * GW;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL((lr_reduce_kernel<E>), dim3((unsigned)grid), dim3(256), 0, s, dzp, dUp,
+                     (E *)a.dz, (E *)a.dU, N, a.R, (int)p.rpad, (int)p.ncb, GW,
+                     (int)(a.B * p.nchunk));
+  return hipGetLastError();
+}
+
+// one 16-row rank block: the argument checks admit R <= 16 only
+template <typename E, int W, int GPV, bool BWD>
+static hipError_t lr_rb(const LrArgs &a) {
+  if constexpr (BWD) {
+    return launch_lr_bwd<E, W, GPV, 1>(a);
+  } else {
+    return a.act ? launch_lr_fwd<E, W, GPV, true, 1>(a) : launch_lr_fwd<E, W, GPV, false, 1>(a);
+  }
+}
+
+template <typename E, int W, bool BWD>
+static hipError_t lr_gpv(const LrArgs &a) {
+  constexpr int V = Vw<E>::n;
+  switch (V / a.H) {
+    case 1: return lr_rb<E, W, 1, BWD>(a);
+    case 2: return lr_rb<E, W, 2, BWD>(a);
+    case 4: return lr_rb<E, W, 4, BWD>(a);
+    default:
+      if constexpr (V == 8) return lr_rb<E, W, 8, BWD>(a);
+      return hipErrorInvalidValue;
+  }
+}
+
+template <typename E, bool BWD>
+hipError_t lr_dispatch(const LrArgs &a) {
+  switch (a.W) {
+    case 1: return lr_gpv<E, 1, BWD>(a);
+    case 2: return lr_gpv<E, 2, BWD>(a);
+    case 3: return lr_gpv<E, 3, BWD>(a);
+    case 4: return lr_gpv<E, 4, BWD>(a);
+    case 5: return lr_gpv<E, 5, BWD>(a);
+    case 6: return lr_gpv<E, 6, BWD>(a);
+    case 7: return lr_gpv<E, 7, BWD>(a);
+    case 8: return lr_gpv<E, 8, BWD>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dsc

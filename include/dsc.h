@@ -43,7 +43,7 @@
  *                        pointer for a non-empty tensor, a pointer not 16-byte
  *                        aligned, an output overlapping another tensor of the
  *                        call, or an element count above 2^62;
- *   DSC_ERR_UNSUPPORTED  W outside 1..8, R outside 1..64, an unknown flag or
+ *   DSC_ERR_UNSUPPORTED  W outside 1..8, R outside 1..16, an unknown flag or
  *                        dtype, or a tying factor H the kernels do not tile
  *                        (head-wise: H divides the vector width, or H is the
  *                        vector width times a power of two up to 64; low-rank:

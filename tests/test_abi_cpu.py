@@ -111,7 +111,7 @@ def test_empty_is_ok_and_queues_nothing(lib):
 def test_lowrank_checks(lib):
     assert lr(lib, H=16, D=64) == UNSUP
     assert lr(lib, R=0) == UNSUP
-    assert lr(lib, R=65) == UNSUP
+    assert lr(lib, R=17) == UNSUP
     assert lr(lib, U=0) == INVALID
     assert lr(lib, y=A + BIG + 8) == INVALID                 # y overlaps z
     assert lr(lib, H=3, D=48, dt=0) == UNSUP
