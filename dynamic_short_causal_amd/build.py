@@ -2,10 +2,13 @@
 
 Every source is compiled for gfx950 only.  Packed-fp32 instruction selection
 is switched off for all device code.  Objects go to ``_build/`` at the
-repository root; the library lands next to this file.
+repository root; the library lands next to this file.  The compiler's
+per-kernel resource report is kept in ``_build/kernel_resources.txt`` and the
+build fails if any kernel spills registers to scratch memory.
 """
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -21,7 +24,8 @@ SOURCES = ["dsc_abi.cpp", "headwise.hip", "lowrank.hip", "lowrank_fwd_bf16.hip",
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
+         "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
+         "-Rpass-analysis=kernel-resource-usage"]
 
 
 def _compile(src):
@@ -31,10 +35,31 @@ def _compile(src):
     cmd = [HIPCC, *FLAGS, *lang, "-c", path, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    lines = [l for l in r.stderr.splitlines() if noise not in l]
+    remarks = [l for l in lines if "kernel-resource-usage" in l]
+    # drop the remarks and their source-context lines ("  37 |  ...", "     | ^")
+    err = "\n".join(l for l in lines if "kernel-resource-usage" not in l
+                    and not re.match(r"^\s*\d*\s*\|", l)
+                    and not l.startswith("In file included from"))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
-    return out, err
+    return out, err, remarks
+
+
+def _resources(remarks):
+    """(kernel, vgprs, agprs, scratch bytes per lane, waves per SIMD) rows."""
+    rows, cur = [], None
+    for l in remarks:
+        m = re.search(r"remark:\s+(.*?):\s*(\S+)\s+\[-Rpass", l)
+        if not m:
+            continue
+        key, val = m.group(1).strip(), m.group(2)
+        if key == "Function Name":
+            cur = {"name": val}
+            rows.append(cur)
+        elif cur is not None:
+            cur[key] = val
+    return rows
 
 
 def build(jobs=None):
@@ -43,10 +68,19 @@ def build(jobs=None):
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         results = list(ex.map(_compile, SOURCES))
-    for _, err in results:
+    for _, err, _ in results:
         if err.strip():
             print(err, file=sys.stderr)
-    objs = [o for o, _ in results]
+    rows = [r for _, _, rem in results for r in _resources(rem)]
+    with open(os.path.join(OBJ, "kernel_resources.txt"), "w") as f:
+        for r in rows:
+            f.write(f"{r['name']} vgpr={r.get('VGPRs')} agpr={r.get('AGPRs')} "
+                    f"scratch={r.get('ScratchSize [bytes/lane]')} "
+                    f"waves_per_simd={r.get('Occupancy [waves/SIMD]')}\n")
+    spills = [r["name"] for r in rows if r.get("ScratchSize [bytes/lane]", "0") != "0"]
+    if spills:
+        raise RuntimeError(f"{len(spills)} kernels spill to scratch, e.g. {spills[:3]}")
+    objs = [o for o, _, _ in results]
     tmp = LIB + ".tmp"
     subprocess.run([HIPCC, "-shared", "--offload-arch=gfx950", "-fPIC", *objs, "-o", tmp],
                    check=True)

@@ -47,7 +47,7 @@ inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int 
   LrBwdPlan p{};
   p.V = bf16 ? 8 : 4;
   p.gpv = p.V / H;
-  const int numax = W <= 5 ? 4 : W <= 7 ? 2 : 1;  // must match LrGeo::NU
+  const int numax = W <= 3 ? 4 : W <= 6 ? 2 : 1;  // must match LrGeo::NU
   p.units = H < numax ? H : numax;   // channel vectors per lane
   p.cb = (int64_t)4 /*waves*/ * 4 /*quarters*/ * p.units * p.V;
   p.ncb = (D + p.cb - 1) / p.cb;

@@ -36,6 +36,7 @@
 //     once per chunk as an fp32 partial.
 // A second kernel adds the partials in a fixed order (deterministic).
 #pragma once
+#include <type_traits>
 #include "dsc_device.hpp"
 #include "dsc_launch.hpp"
 
@@ -52,7 +53,7 @@ template <typename E, int W, int GPV> struct LrGeo {
   static constexpr int V = Vw<E>::n;
   static constexpr int H = V / GPV;         // channels per filter group
   // channel vectors per lane: up to 4, fewer for wide filters (register budget)
-  static constexpr int NUMAX = W <= 5 ? 4 : W <= 7 ? 2 : 1;
+  static constexpr int NUMAX = W <= 3 ? 4 : W <= 6 ? 2 : 1;
   static constexpr int NU = H < NUMAX ? H : NUMAX;
   static constexpr int NG = NU * GPV;       // (group, vector) instances per lane per tap
   static constexpr int NP = (NG + 3) / 4;   // filter MFMAs per tap (4 rows per lane each)
@@ -83,36 +84,55 @@ __device__ __forceinline__ f32x4 mma_dz(typename DzFrag<BF>::T a, typename DzFra
   else return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// lane l <- lane l+k of the same 16-lane row (0 past the row end)
-__device__ __forceinline__ float row_shl(float v, int k) {
-  int x = __float_as_int(v), r = 0;
-  switch (k) {
-    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x101, 0xF, 0xF, true); break;
-    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x102, 0xF, 0xF, true); break;
-    case 3: r = __builtin_amdgcn_update_dpp(0, x, 0x103, 0xF, 0xF, true); break;
-    case 4: r = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xF, 0xF, true); break;
-    case 5: r = __builtin_amdgcn_update_dpp(0, x, 0x105, 0xF, 0xF, true); break;
-    case 6: r = __builtin_amdgcn_update_dpp(0, x, 0x106, 0xF, 0xF, true); break;
-    case 7: r = __builtin_amdgcn_update_dpp(0, x, 0x107, 0xF, 0xF, true); break;
-    default: r = x; break;
-  }
-  return __int_as_float(r);
+// DPP row shifts inside each 16-lane row, with 0 where the source lane falls
+// outside the row.  k is a compile-time constant after unrolling.
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
-// lane l <- lane l-(16-k) of the same 16-lane row (0 before the row start):
-// lanes 16-k..15 receive lanes 0..k-1
-__device__ __forceinline__ float row_shr_16mk(float v, int k) {
-  int x = __float_as_int(v), r = 0;
+// lane l <- lane l+k
+__device__ __forceinline__ uint32_t row_shl_u32(uint32_t v, int k) {
   switch (k) {
-    case 1: r = __builtin_amdgcn_update_dpp(0, x, 0x11F, 0xF, 0xF, true); break;
-    case 2: r = __builtin_amdgcn_update_dpp(0, x, 0x11E, 0xF, 0xF, true); break;
-    case 3: r = __builtin_amdgcn_update_dpp(0, x, 0x11D, 0xF, 0xF, true); break;
-    case 4: r = __builtin_amdgcn_update_dpp(0, x, 0x11C, 0xF, 0xF, true); break;
-    case 5: r = __builtin_amdgcn_update_dpp(0, x, 0x11B, 0xF, 0xF, true); break;
-    case 6: r = __builtin_amdgcn_update_dpp(0, x, 0x11A, 0xF, 0xF, true); break;
-    case 7: r = __builtin_amdgcn_update_dpp(0, x, 0x119, 0xF, 0xF, true); break;
-    default: r = 0; break;
+    case 1: return dpp_u32<0x101>(v);  case 2: return dpp_u32<0x102>(v);
+    case 3: return dpp_u32<0x103>(v);  case 4: return dpp_u32<0x104>(v);
+    case 5: return dpp_u32<0x105>(v);  case 6: return dpp_u32<0x106>(v);
+    case 7: return dpp_u32<0x107>(v);  case 8: return dpp_u32<0x108>(v);
+    case 9: return dpp_u32<0x109>(v);  case 10: return dpp_u32<0x10A>(v);
+    case 11: return dpp_u32<0x10B>(v); case 12: return dpp_u32<0x10C>(v);
+    case 13: return dpp_u32<0x10D>(v); case 14: return dpp_u32<0x10E>(v);
+    case 15: return dpp_u32<0x10F>(v); default: return v;
   }
-  return __int_as_float(r);
+}
+// lane l <- lane l-k
+__device__ __forceinline__ uint32_t row_shr_u32(uint32_t v, int k) {
+  switch (k) {
+    case 1: return dpp_u32<0x111>(v);  case 2: return dpp_u32<0x112>(v);
+    case 3: return dpp_u32<0x113>(v);  case 4: return dpp_u32<0x114>(v);
+    case 5: return dpp_u32<0x115>(v);  case 6: return dpp_u32<0x116>(v);
+    case 7: return dpp_u32<0x117>(v);  case 8: return dpp_u32<0x118>(v);
+    case 9: return dpp_u32<0x119>(v);  case 10: return dpp_u32<0x11A>(v);
+    case 11: return dpp_u32<0x11B>(v); case 12: return dpp_u32<0x11C>(v);
+    case 13: return dpp_u32<0x11D>(v); case 14: return dpp_u32<0x11E>(v);
+    case 15: return dpp_u32<0x11F>(v); default: return v;
+  }
+}
+__device__ __forceinline__ float row_shl(float v, int k) {
+  return __uint_as_float(row_shl_u32(__float_as_uint(v), k));
+}
+// lanes 16-k..15 receive lanes 0..k-1 (row shift right by 16-k)
+__device__ __forceinline__ float row_shr_16mk(float v, int k) {
+  return __uint_as_float(row_shr_u32(__float_as_uint(v), 16 - k));
+}
+// Tap k of a 16-token tile held one token per lane: lane j gets the vector of
+// token t+j-k, from lane j-k of this tile or lane 16-k+j of the previous one.
+__device__ __forceinline__ uint4 tap_vec(uint4 cur, uint4 prev, int k) {
+  if (k == 0) return cur;
+  return make_uint4(row_shr_u32(cur.x, k) | row_shl_u32(prev.x, 16 - k),
+                    row_shr_u32(cur.y, k) | row_shl_u32(prev.y, 16 - k),
+                    row_shr_u32(cur.z, k) | row_shl_u32(prev.z, 16 - k),
+                    row_shr_u32(cur.w, k) | row_shl_u32(prev.w, 16 - k));
+}
+__device__ __forceinline__ uint4 sel4(bool ok, uint4 v) {
+  return ok ? v : make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Filter slot sigma = k*NG + m of lane quarter qq; m = u*GPV + gi names vector
@@ -160,33 +180,32 @@ __device__ __forceinline__ void load_wA(const E *__restrict__ U, int GW, int R, 
 }
 
 // B operand of the filter MFMAs: z^T of token `tok` (lane (q, j) holds ranks
-// of K-quarter q), zero for an invalid token.
+// of K-quarter q).  Branch-free so it can be issued a tile ahead: a lane with
+// no token (`valid` false) reads the first z row instead.  Such lanes' filters
+// are never used for an output, and ranks r >= R meet zero rows of U, so the
+// fragment needs no masking.
 template <typename E, int KS>
 __device__ __forceinline__ void load_zB(const E *__restrict__ z, int64_t tok, bool valid, int R,
                                         int q, typename WFrag<sizeof(E) == 2>::T (&bz)[KS]) {
   constexpr bool BF = sizeof(E) == 2;
-  const E *zr = z + tok * R;
+  const E *zr = z + (valid ? tok * R : 0);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if constexpr (BF) {
       const int r0 = ks * 16 + 4 * q;
-      s16x4 f = {0, 0, 0, 0};
-      if (valid) {
-        if ((R & 3) == 0) {
-          if (r0 < R) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(zr + r0);
-            f[0] = (short)(v.x & 0xffff); f[1] = (short)(v.x >> 16);
-            f[2] = (short)(v.y & 0xffff); f[3] = (short)(v.y >> 16);
-          }
-        } else {
+      s16x4 f;
+      if ((R & 3) == 0) {  // 8-byte aligned 4-rank groups, all in or all out
+        const uint2 v = *reinterpret_cast<const uint2 *>(r0 < R ? zr + r0 : z);
+        f[0] = (short)(v.x & 0xffff); f[1] = (short)(v.x >> 16);
+        f[2] = (short)(v.y & 0xffff); f[3] = (short)(v.y >> 16);
+      } else {
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) f[e2] = (r0 + e2 < R) ? (short)zr[r0 + e2] : (short)0;
-        }
+        for (int e2 = 0; e2 < 4; ++e2) f[e2] = (short)(r0 + e2 < R ? zr[r0 + e2] : z[0]);
       }
       bz[ks] = f;
     } else {
       const int r = ks * 4 + q;
-      bz[ks] = (valid && r < R) ? (float)zr[r] : 0.f;
+      bz[ks] = r < R ? zr[r] : z[0];
     }
   }
 }
@@ -233,28 +252,50 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
   load_wA<E, W, GPV, KS>(U, GW, R, cw, D, lane, aw);
 
   const int64_t seq = (int64_t)b * T;
+  // Each lane loads only the x row of its own token (one 16-byte vector per
+  // unit); taps k >= 1 come from the neighbouring lanes by DPP (tap_vec), the
+  // first W-1 lanes of a tile from the previous tile's registers.  Loads are
+  // issued one tile ahead and are branch-free: a lane without a token or
+  // channel reads row 0 and zeroes it on use.
+  typename WFrag<Gm::BF>::T zn[KS];
+  uint4 xn[NU], xp[NU];
+  auto issue = [&](int t) {
+    const int tau = t + j;
+    const bool valid = tau < t1;
+    load_zB<E, KS>(z, seq + tau, valid, R, q, zn);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c = cw + (u * 4 + q) * V;
+      xn[u] = ld16(x + (valid && c < D ? (seq + tau) * D + c : 0));
+    }
+  };
+  // the 16 tokens before the chunk (zero before the sequence start)
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int c = cw + (u * 4 + q) * V;
+    const int tb = t0 - 16 + j;
+    const bool ok = tb >= 0 && c < D;
+    xp[u] = sel4(ok, ld16(x + (ok ? (seq + tb) * D + c : 0)));
+  }
+  issue(t0);
   for (int t = t0; t < t1; t += 16) {
     const int tau = t + j;
     const bool valid = tau < t1;
     typename WFrag<Gm::BF>::T bz[KS];
-    load_zB<E, KS>(z, seq + tau, valid, R, q, bz);
+    uint4 xc[NU];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bz[ks] = zn[ks];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) xc[u] = sel4(valid && cw + (u * 4 + q) * V < D, xn[u]);
+    if (t + 16 < t1) issue(t + 16);  // wave-uniform
     f32x4 wacc[W][NP];
     gen_filters<E, W, GPV, KS>(aw, bz, wacc);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int c = cw + (u * 4 + q) * V;
-      if (!valid || c >= D) continue;
-      const E *xp = x + (seq + tau) * D + c;
       float xk[W][V];
 #pragma unroll
-      for (int k = 0; k < W; ++k) {
-        if (tau - k >= 0) {
-          unpack<E>(ld16(xp - (int64_t)k * D), xk[k]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < V; ++i) xk[k][i] = 0.f;
-        }
-      }
+      for (int k = 0; k < W; ++k) unpack<E>(tap_vec(xc[u], xp[u], k), xk[k]);
       float o[V];
 #pragma unroll
       for (int i = 0; i < V; ++i) {
@@ -265,7 +306,8 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
         if constexpr (ACT) s = silu_f(s);
         o[i] = fmaf(rho, xk[0][i], s);
       }
-      st16(y + (seq + tau) * D + c, pack<E>(o));
+      if (valid && c < D) st16(y + (seq + tau) * D + c, pack<E>(o));
+      xp[u] = xc[u];
     }
   }
 }
@@ -275,15 +317,34 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
 // ---------------------------------------------------------------------------
 template <typename E, int W, int GPV, int RB> struct LrBwdSmem {
   using Gm = LrGeo<E, W, GPV>;
-  // per wave: dw^T, 4*NS slot rows x 16 tokens
-  static constexpr int dwt_bytes = 4 * Gm::NS * 16 * (int)sizeof(E);
+  // per wave: dw^T, 4*NS slot rows x 16 tokens, padded with zero rows to
+  // whole 16-row MFMA blocks
+  static constexpr int nrb = (Gm::NS + 3) / 4;
+  static constexpr int dwt_bytes = 16 * nrb * 16 * (int)sizeof(E);
   // per workgroup: two buffers of the 4 waves' dz^T tiles (RB x 64 lanes x 4)
   static constexpr int dz_floats = 2 * 4 * RB * 64 * 4;
   static constexpr int bytes = 4 * dwt_bytes + dz_floats * 4;
 };
 
+// Two waves per SIMD (at most 256 VGPR+AGPR per lane) where the compiler fits
+// that without spilling, one otherwise.  The set was read off the kernel
+// resource-usage report of every instance.
+template <typename E, int W, int GPV>
+constexpr int lr_bwd_min_waves() {
+  if constexpr (sizeof(E) == 2) {
+    const bool two = W == 1 || ((W == 2 || W == 3) && GPV == 4) ||
+                     (W == 4 && (GPV == 1 || GPV == 8)) || (W == 5 && GPV == 8) ||
+                     (W == 7 && (GPV == 1 || GPV == 2));
+    return two ? 2 : 1;
+  } else {
+    const bool two = W <= 4 || (W == 5 && (GPV == 1 || GPV == 4)) ||
+                     (W == 7 && (GPV == 1 || GPV == 2)) || (W == 8 && GPV == 1);
+    return two ? 2 : 1;
+  }
+}
+
 template <typename E, int W, int GPV, int RB>
-__global__ __launch_bounds__(kLrThreads) void lr_bwd_kernel(
+__global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void lr_bwd_kernel(
     const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U,
     const E *__restrict__ dy, E *__restrict__ dx, float *__restrict__ dzp,
     float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk, int ncb, int64_t N,
@@ -295,7 +356,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_bwd_kernel(
   constexpr int V = Gm::V, NU = Gm::NU, NG = Gm::NG, NP = Gm::NP, NS = Gm::NS;
   constexpr int KS = RB * (BF ? 1 : 4);
   constexpr int NDZ = BF ? (NS + 7) / 8 : NS;  // dz MFMAs per tile and rank block
-  constexpr int NRB = NS / 4;                  // 16-row blocks of the wave's 4*NS slots
+  constexpr int NRB = Sm::nrb;                 // 16-row blocks of the wave's 4*NS slots
   constexpr int RP = 16 * RB;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -311,6 +372,8 @@ __global__ __launch_bounds__(kLrThreads) void lr_bwd_kernel(
   const int64_t seq = (int64_t)b * T;
 
   E *dwt = reinterpret_cast<E *>(smem + wave * Sm::dwt_bytes);
+  // rows 4*NS .. 16*NRB-1 pad the last MFMA block and stay zero
+  for (int r = 4 * NS + (lane >> 4); r < 16 * NRB; r += 4) dwt[r * 16 + (lane & 15)] = (E)0;
   float *dzbuf = reinterpret_cast<float *>(smem + 4 * Sm::dwt_bytes);
 
   // resident operands: filter A fragments and dz A fragments (U columns)
@@ -354,6 +417,50 @@ __global__ __launch_bounds__(kLrThreads) void lr_bwd_kernel(
   const int tiles = (t1 - t0 + 15) / 16;
   const int nsteps = tiles + (t1 < T ? 1 : 0);  // + a halo tile when tokens follow the chunk
 
+  // Loads of one step, issued a step ahead and branch-free: a lane without a
+  // token (past T) or a channel (past D) reads row 0 instead, and the value is
+  // zeroed where it is used, so every lane runs the same instructions and the
+  // DPP row shifts below always see defined data.
+  typename WFrag<BF>::T zn[KS];
+  uint4 dyn[NU], xn[NU], xp[NU];
+  typedef typename std::conditional<BF, short, float>::type zt_t;
+  zt_t ztn[4];  // z[t + 4qa + e][n]: the dU B operand (K = tokens)
+  auto issue = [&](int st) {
+    const int t = t0 + 16 * st;
+    const bool halo = st == tiles;
+    const int tau = t + j;
+    const bool in_seq = tau < T;
+    load_zB<E, KS>(z, seq + tau, in_seq, R, q, zn);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c = cw + (u * 4 + q) * V;
+      const bool act_lane = in_seq && c < D;
+      const int64_t off = act_lane ? (seq + tau) * D + c : 0;
+      dyn[u] = ld16(dy + off);
+      if (ACT || !halo) xn[u] = ld16(x + off);  // own row; taps come by DPP
+    }
+    if (!halo) {
+      const int qa = lane >> 4, n = lane & 15;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int tk = BF ? t + 4 * qa + e2 : t + 4 * e2 + qa;
+        const bool ok = tk < t1 && n < R;
+        const E v = z[ok ? (seq + tk) * R + n : 0];
+        if constexpr (BF) ztn[e2] = ok ? (short)v : (short)0;
+        else ztn[e2] = ok ? (float)v : 0.f;
+      }
+    }
+  };
+  // x of the 16 tokens before the chunk (zero before the sequence start)
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int c = cw + (u * 4 + q) * V;
+    const int tb = t0 - 16 + j;
+    const bool ok = tb >= 0 && c < D;
+    xp[u] = sel4(ok, ld16(x + (ok ? (seq + tb) * D + c : 0)));
+  }
+  issue(0);
+
   for (int st = 0; st < nsteps; ++st) {
     const int t = t0 + 16 * st;
     const bool halo = st == tiles;  // wave-uniform
@@ -362,31 +469,36 @@ __global__ __launch_bounds__(kLrThreads) void lr_bwd_kernel(
     const bool in_chunk = !halo && tau < t1;
 
     typename WFrag<BF>::T bz[KS];
-    load_zB<E, KS>(z, seq + tau, in_seq, R, q, bz);
+    uint4 dyr[NU], xc[NU];
+    zt_t zt[4];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bz[ks] = zn[ks];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const bool act_lane = in_seq && cw + (u * 4 + q) * V < D;
+      dyr[u] = dyn[u];
+      xc[u] = sel4(act_lane && (ACT || !halo), xn[u]);
+    }
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) zt[e2] = ztn[e2];
+    if (st + 1 < nsteps) issue(st + 1);
+
     f32x4 wacc[W][NP];
     gen_filters<E, W, GPV, KS>(aw, bz, wacc);
 
-    // Branch-free per lane: an invalid lane (token past T or channel past D)
-    // reads a valid dummy address and zeroes the value, so every lane runs the
-    // same instructions and the DPP row shifts below see defined data.
     const int tp = t - 16 + j;  // token of the previous tile held by this lane
     float dwv[NS];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int c = cw + (u * 4 + q) * V;
       const bool act_lane = in_seq && c < D;
-      const int64_t off = act_lane ? (seq + tau) * D + c : 0;
       float dyv[V];
-      unpack<E>(ld16(dy + off), dyv);
+      unpack<E>(dyr[u], dyv);
 #pragma unroll
       for (int i = 0; i < V; ++i) dyv[i] = act_lane ? dyv[i] : 0.f;
-      // x tap k of this vector (zero before the sequence start)
-      auto xtap = [&](int k, float (&o)[V]) {
-        const bool ok = act_lane && tau - k >= 0;
-        unpack<E>(ld16(x + (ok ? off - (int64_t)k * D : 0)), o);
-#pragma unroll
-        for (int i = 0; i < V; ++i) o[i] = ok ? o[i] : 0.f;
-      };
+      // x tap k of this vector: token tau-k, by DPP from the lanes (and the
+      // previous tile) that loaded it; zero before the sequence start
+      auto xtap = [&](int k, float (&o)[V]) { unpack<E>(tap_vec(xc[u], xp[u], k), o); };
       float ds[V];
       if (ACT) {
         float sacc[V];
@@ -439,6 +551,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_bwd_kernel(
           dwv[k * NG + u * GPV + gi] = in_chunk ? a : 0.f;
         }
       }
+      xp[u] = xc[u];
     }
     have_prev = true;
     if (halo) break;
@@ -495,17 +608,11 @@ __global__ __launch_bounds__(kLrThreads) void lr_bwd_kernel(
     __builtin_amdgcn_wave_barrier();
     if constexpr (BF) {
       // B operand: z[token 4qa+e2][16rb + n] (K = tokens)
+      static_assert(RB == 1, "one rank block");
       const int qa = lane >> 4, n = lane & 15;
       s16x4 bzt[RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int r = 16 * rb + n;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int tk = t + 4 * qa + e2;
-          bzt[rb][e2] = (tk < t1 && r < R) ? (short)z[(seq + tk) * R + r] : (short)0;
-        }
-      }
+      for (int e2 = 0; e2 < 4; ++e2) bzt[0][e2] = zt[e2];
 #pragma unroll
       for (int a = 0; a < NRB; ++a) {
         const uint2 v = *reinterpret_cast<const uint2 *>(dwt + (16 * a + n) * 16 + 4 * qa);
@@ -517,16 +624,12 @@ __global__ __launch_bounds__(kLrThreads) void lr_bwd_kernel(
           accU[a][rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(af, bzt[rb], accU[a][rb], 0, 0, 0);
       }
     } else {
+      static_assert(RB == 1, "one rank block");
       const int qa = lane >> 4, n = lane & 15;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const int tk = t + 4 * s4 + qa;
         float bzt[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int r = 16 * rb + n;
-          bzt[rb] = (tk < t1 && r < R) ? (float)z[(seq + tk) * R + r] : 0.f;
-        }
+        bzt[0] = zt[s4];
 #pragma unroll
         for (int a = 0; a < NRB; ++a) {
           const float af = dwt[(16 * a + n) * 16 + 4 * s4 + qa];
@@ -557,6 +660,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_bwd_kernel(
 #pragma unroll
     for (int a = 0; a < NRB; ++a) {
       const int sg = 4 * a + qo;
+      if (sg >= NS) continue;  // padding rows of the last block
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int col = slot_col<E, W, GPV>(cw, e, sg / NG, sg % NG, D);

@@ -167,3 +167,11 @@ def test_full_size_qkv_lowrank(dsc, orc):
 def test_full_size_rnn_lowrank_silu(dsc, orc):
     """B=16, T=4096, D=4608, W=4, R=16, H=8, SiLU."""
     _full_size(dsc, orc, di.WORKLOADS["rnn_lowrank_silu"], 24, 12)
+
+
+@pytest.mark.parametrize("W,H,dt", [(7, 8, "bf16"), (7, 4, "bf16"), (5, 8, "bf16"),
+                                    (5, 4, "f32"), (7, 4, "f32"), (6, 2, "f32")])
+def test_slot_counts_not_multiple_of_four(dsc, orc, W, H, dt):
+    """Shapes whose per-lane filter-slot count leaves a partial dU MFMA block."""
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    run_case(dsc, orc, 2, 40, 512, W, H, 16, dtype, True, True, 8300 + 10 * W + H)
