@@ -13,6 +13,8 @@ kernels run on), and the fp64 CPU oracle timed on a bounded sample of the same
 workload on this host (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --profile-ops K   (K untimed passes of every op plus a
+                                          512 MiB device copy, for rocprofv3)
 """
 import argparse
 import hashlib
@@ -117,6 +119,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-ops", type=int, default=0,
+                    help="run each op this many times (and a copy of known size), no timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -167,6 +171,18 @@ def main():
             ops[n]()
             if events is not None:
                 events[i][1].record(stream)
+
+    if args.profile_ops:
+        # counter runs: the 512 MiB copy (read and write of known size) calibrates
+        # FETCH_SIZE / WRITE_SIZE against the bytes actually moved
+        src = torch.empty(1 << 28, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.profile_ops):
+            step()
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("bench: profile passes done", file=sys.stderr, flush=True)
+        return
 
     print("bench: warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
