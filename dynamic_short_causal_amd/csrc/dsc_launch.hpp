@@ -42,6 +42,26 @@ struct LrBwdPlan {
   size_t bytes;     // total workspace
 };
 
+// Token-chunk length of a (batch, chunk, channel block) grid.  Long chunks
+// amortise per-workgroup set-up and keep the partial sums few; the grid should
+// also fill whole rounds of `resident` concurrent workgroups (MI355X: 256
+// CUs), since a last, partial round leaves CUs idle.  Picks the longest power
+// of two in 64..2048 whose rounds are at least 90 % full, else the fullest.
+inline int pick_chunk(int64_t B, int64_t T, int64_t ncb, int64_t resident) {
+  int best = 64;
+  double best_eff = -1.0;
+  for (int tc = 2048; tc >= 64; tc /= 2) {
+    const int64_t wg = B * ((T + tc - 1) / tc) * ncb;
+    if (wg <= 0) return (int)((T + 15) / 16 * 16);
+    const int64_t rounds = (wg + resident - 1) / resident;
+    const double eff = (double)wg / (double)(rounds * resident);
+    if (eff >= 0.9) { best = tc; break; }
+    if (eff > best_eff + 1e-9) { best_eff = eff; best = tc; }
+  }
+  if (T < best) best = (int)((T + 15) / 16 * 16);
+  return best < 16 ? 16 : best;
+}
+
 inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int R,
                              bool bf16) {
   LrBwdPlan p{};
@@ -52,14 +72,8 @@ inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int 
   p.cb = (int64_t)4 /*waves*/ * 4 /*quarters*/ * p.units * p.V;
   p.ncb = (D + p.cb - 1) / p.cb;
   p.rpad = 16;  // R <= 16: one 16-row MFMA block of ranks
-  // Long chunks keep the dU partials small; enough workgroups to fill the
-  // chip (>= 2 per CU) bound the length from above.
-  int tc = 1024;
-  while (tc > 16 && B * ((T + tc - 1) / tc) * p.ncb < 512) tc /= 2;
-  if (T < tc) tc = (int)((T + 15) / 16 * 16);
-  if (tc < 16) tc = 16;
-  p.tc = tc;
-  p.nchunk = (T + tc - 1) / tc;
+  p.tc = pick_chunk(B, T, p.ncb, 512);  // 2 resident workgroups per CU
+  p.nchunk = (T + p.tc - 1) / p.tc;
   const int64_t G = D / H;
   p.dz_part = (size_t)p.ncb * (size_t)(B * T) * (size_t)p.rpad * 4;
   p.dU_part = (size_t)(B * p.nchunk) * (size_t)p.rpad * (size_t)(G * W) * 4;

@@ -7,23 +7,24 @@
 
 namespace dsc {
 
-template <typename E, int W, int GPV, bool ACT, int RB>
+template <typename E, int W, int GPV, bool ACT>
 static hipError_t launch_lr_fwd(const LrArgs &a) {
   using Gm = LrGeo<E, W, GPV>;
   hipStream_t s = (hipStream_t)a.stream;
   const float rho = a.residual ? 1.f : 0.f;
-  const int TC = a.T >= 256 ? 256 : (int)((a.T + 15) / 16 * 16);
-  const int nchunk = (int)((a.T + TC - 1) / TC);
   const int ncb = (int)((a.D + Gm::CB - 1) / Gm::CB);
+  const int TC = pick_chunk(a.B, a.T, ncb, 768);  // 3 resident workgroups per CU
+  const int nchunk = (int)((a.T + TC - 1) / TC);
   const int64_t nblocks = a.B * nchunk * (int64_t)ncb;
   if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((lr_fwd_kernel<E, W, GPV, ACT, RB>), dim3((unsigned)nblocks),
-                     dim3(kLrThreads), 0, s, (const E *)a.x, (const E *)a.z, (const E *)a.U,
-                     (E *)a.y, (int)a.T, (int)a.D, a.R, TC, nchunk, ncb, rho);
+  constexpr int smem = LrFwdSmem<E, W, GPV>::bytes;
+  hipLaunchKernelGGL((lr_fwd_kernel<E, W, GPV, ACT>), dim3((unsigned)nblocks),
+                     dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
+                     (const E *)a.U, (E *)a.y, (int)a.T, (int)a.D, a.R, TC, nchunk, ncb, rho);
   return hipGetLastError();
 }
 
-template <typename E, int W, int GPV, int RB>
+template <typename E, int W, int GPV>
 static hipError_t launch_lr_bwd(const LrArgs &a) {
   hipStream_t s = (hipStream_t)a.stream;
   const float rho = a.residual ? 1.f : 0.f;
@@ -34,8 +35,8 @@ static hipError_t launch_lr_bwd(const LrArgs &a) {
   float *dUp = (float *)((char *)a.ws + p.dz_part);
   const int64_t nblocks = a.B * p.nchunk * p.ncb;
   if (nblocks > 0) {
-    using Sm = LrBwdSmem<E, W, GPV, RB>;
-    hipLaunchKernelGGL((lr_bwd_kernel<E, W, GPV, RB>), dim3((unsigned)nblocks),
+    using Sm = LrBwdSmem<E, W, GPV>;
+    hipLaunchKernelGGL((lr_bwd_kernel<E, W, GPV>), dim3((unsigned)nblocks),
                        dim3(kLrThreads), Sm::bytes, s, (const E *)a.x, (const E *)a.z,
                        (const E *)a.U, (const E *)a.dy, (E *)a.dx, dzp, dUp, (int)a.T, (int)a.D,
                        a.R, p.tc, (int)p.nchunk, (int)p.ncb, N, rho, a.act ? 1 : 0);
@@ -56,9 +57,9 @@ static hipError_t launch_lr_bwd(const LrArgs &a) {
 template <typename E, int W, int GPV, bool BWD>
 static hipError_t lr_rb(const LrArgs &a) {
   if constexpr (BWD) {
-    return launch_lr_bwd<E, W, GPV, 1>(a);
+    return launch_lr_bwd<E, W, GPV>(a);
   } else {
-    return a.act ? launch_lr_fwd<E, W, GPV, true, 1>(a) : launch_lr_fwd<E, W, GPV, false, 1>(a);
+    return a.act ? launch_lr_fwd<E, W, GPV, true>(a) : launch_lr_fwd<E, W, GPV, false>(a);
   }
 }
 
