@@ -22,10 +22,12 @@
 // v_mfma_f32_16x16x16_bf16 (bf16 products, fp32 sums); fp32 uses
 // v_mfma_f32_16x16x4_f32.
 //
-// Shifted rows.  Each lane loads only its own token's rows; the rows of other
-// tokens (x at t-k for the taps, ds at t+k for dx) go through a wave-private
-// 32-row LDS ring, written once per tile and read back with 16-byte LDS
-// reads, so the shifts cost LDS bandwidth rather than vector-ALU issue.
+// Shifted rows.  The rows of other tokens (x at t-k for the taps, ds at t+k
+// for dx) go through a 32-row LDS ring, written once per tile and read back
+// with 16-byte LDS reads, so the shifts cost LDS bandwidth rather than
+// vector-ALU issue.  The forward's ring spans the workgroup and is filled by
+// row-major loads; its outputs leave through an LDS staging tile, so every
+// device-memory access is a whole-row segment of the channel block.
 //
 // Backward per tile (one-tile lag for dx):
 //   * ds = dy (or dy * SiLU'(s), s recomputed from the on-chip filters);
@@ -191,9 +193,22 @@ __device__ __forceinline__ void gen_tap(
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <typename E, int W, int GPV> struct LrFwdSmem {
-  // per wave: 32 token rows of x in fp32 (the ring row of the backward's ds)
-  static constexpr int bytes = 4 * 32 * LrGeo<E, W, GPV>::DROW;
+// Device memory is touched only by whole-workgroup row segments: per tile the
+// workgroup loads the 16 x CB slab of x (thread -> one 16-byte vector of a
+// row, consecutive threads along the row) into a workgroup-wide fp32 ring of
+// 32 token rows, the lanes compute in the token-per-lane layout reading the
+// ring, and the 16 x CB slab of y goes back through an LDS staging tile with
+// the same row-major thread mapping.  Loading and storing per lane (16 token
+// rows of 64 bytes per instruction) ran at two thirds of this speed.
+template <typename E, int W, int GPV> struct LrFwdGeo {
+  using Gm = LrGeo<E, W, GPV>;
+  static constexpr int XR = Gm::CB * 4 + 16;               // ring row pitch (fp32)
+  static constexpr int SP = Gm::CB * (int)sizeof(E) + 16;  // staging row pitch
+  static constexpr int VPR = Gm::CB / Gm::V;               // 16-byte vectors per row
+  static constexpr int RPP = kLrThreads / VPR;             // rows per cooperative pass
+  static constexpr int NPASS = 16 / RPP;                   // passes per 16-row slab
+  static_assert(RPP * NPASS == 16, "a slab is a whole number of passes");
+  static constexpr int bytes = 32 * XR + 16 * SP;
 };
 
 template <typename E, int W, int GPV, bool ACT>
@@ -201,9 +216,12 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
     const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U, E *__restrict__ y,
     int T, int D, int R, int TC, int nchunk, int ncb, float rho) {
   using Gm = LrGeo<E, W, GPV>;
-  constexpr int V = Gm::V, NU = Gm::NU, NP = Gm::NP, KS = Gm::KS, DROW = Gm::DROW;
+  using Fg = LrFwdGeo<E, W, GPV>;
+  constexpr int V = Gm::V, NU = Gm::NU, NP = Gm::NP, KS = Gm::KS;
+  constexpr int XR = Fg::XR, SP = Fg::SP, VPR = Fg::VPR, RPP = Fg::RPP, NPASS = Fg::NPASS;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, j = lane & 15;
+  unsigned char *ring = smem, *stage = smem + 32 * XR;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, j = lane & 15;
   int bid = blockIdx.x;
   const int cb = bid % ncb;
   bid /= ncb;
@@ -212,86 +230,86 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
   const int cw = cb * Gm::CB + wave * Gm::CW;
   const int t0 = chunk * TC, t1 = min(T, t0 + TC);
   const int GW = (D / Gm::H) * W;
-  unsigned char *xring = smem + wave * 32 * DROW;
-  // x ring (fp32): V values of vector u at token `tok` (any sign; tok & 31 is
-  // tok mod 32), as V/4 16-byte pieces
-  auto xslot = [&](int tok, int u) {
-    return reinterpret_cast<f32x4 *>(xring + (tok & 31) * DROW + (u * 4 + q) * V * 4);
-  };
-  auto put = [&](int tok, int u, const float (&v)[V]) {
+  const int64_t seq = (int64_t)b * T;
+  // row-major role: vector vv of rows rr, rr + RPP, ...
+  const int vv = tid % VPR, rr = tid / VPR;
+  const int cc = cb * Gm::CB + vv * V;
+  const bool cc_ok = cc < D;
+  // ring row slot of token `tok` (any sign): tok & 31 is tok mod 32
+  auto ring_put = [&](int tok, const uint4 &raw, bool ok) {
+    float v[V];
+    unpack<E>(sel4(ok, raw), v);
+    f32x4 *dst = reinterpret_cast<f32x4 *>(ring + (tok & 31) * XR + vv * V * 4);
 #pragma unroll
-    for (int h = 0; h < V / 4; ++h)
-      xslot(tok, u)[h] = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+    for (int h = 0; h < V / 4; ++h) dst[h] = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+  };
+  // the V channels of lane vector u at token `tok`, as V/4 16-byte pieces
+  auto xrow = [&](int tok, int u) {
+    return reinterpret_cast<const f32x4 *>(ring + (tok & 31) * XR +
+                                           (wave * Gm::CW + (u * 4 + q) * V) * 4);
   };
 
   typename WFrag<Gm::BF>::T aw[W][NP][KS];
   load_wA<E, W, GPV>(U, GW, R, cw, D, lane, aw);
 
-  const int64_t seq = (int64_t)b * T;
-  // the 16 rows before the chunk go to the ring (zero before the sequence)
+  // the 16 rows before the chunk (zero before the sequence)
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int c = cw + (u * 4 + q) * V;
-    const int tb = t0 - 16 + j;
-    const bool ok = tb >= 0 && c < D;
-    float v[V];
-    unpack<E>(sel4(ok, ld16(x + (ok ? (seq + tb) * D + c : 0))), v);
-    put(tb, u, v);
+  for (int p = 0; p < NPASS; ++p) {
+    const int tb = t0 - 16 + p * RPP + rr;
+    const bool ok = tb >= 0 && cc_ok;
+    ring_put(tb, ld16(x + (ok ? (seq + tb) * D + cc : 0)), ok);
   }
   // Loads of one tile go to one of PF prefetch slots, PF tiles ahead; they are
-  // branch-free (a lane without a token or channel reads row 0 and zeroes it).
+  // branch-free (a thread without a token or channel reads row 0, zeroed later).
   constexpr int PF = 4;
-  int64_t row0[NU];
-  bool chan_ok[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int c = cw + (u * 4 + q) * V;
-    chan_ok[u] = c < D;
-    row0[u] = (seq + t0 + j) * D + c;
-  }
   typename WFrag<Gm::BF>::T zn[PF][KS];
-  uint4 xn[PF][NU];
+  uint4 xn[PF][NPASS];
   auto issue = [&](int t, int sl) {  // sl: compile-time after unrolling
-    const int tau = t + j;
-    const bool valid = tau < t1;
-    load_zB<E, KS>(z, seq + tau, valid, R, q, zn[sl]);
-    const int64_t step_off = (int64_t)(t - t0) * D;
+    load_zB<E, KS>(z, seq + t + j, t + j < t1, R, q, zn[sl]);
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
-      xn[sl][u] = ld16(x + (valid && chan_ok[u] ? row0[u] + step_off : 0));
+    for (int p = 0; p < NPASS; ++p) {
+      const int tr = t + p * RPP + rr;
+      xn[sl][p] = ld16(x + (tr < t1 && cc_ok ? (seq + tr) * D + cc : 0));
+    }
   };
+  // Per tile: fill the ring rows of the tile; barrier; taps, outputs to the
+  // staging tile; barrier; row-major stores.  The next tile's fill overwrites
+  // the rows of tile t-16, whose last reads precede the second barrier, and
+  // its staging writes follow its own first barrier, after these stores read.
   auto tile = [&](int t, int sl) {
     const int tau = t + j;
-    const bool valid = tau < t1;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int tr = t + p * RPP + rr;
+      ring_put(tr, xn[sl][p], tr < t1 && cc_ok);
+    }
     typename WFrag<Gm::BF>::T bz[KS];
-    float x0[NU][V];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) bz[ks] = zn[sl][ks];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      unpack<E>(sel4(valid && chan_ok[u], xn[sl][u]), x0[u]);
-      put(tau, u, x0[u]);
-    }
-    if (t + 16 * PF < t1) issue(t + 16 * PF, sl);  // wave-uniform
+    if (t + 16 * PF < t1) issue(t + 16 * PF, sl);  // workgroup-uniform
     f32x4 wacc[W][NP];
 #pragma unroll
     for (int k = 0; k < W; ++k) gen_tap<E, W, GPV>(aw[k], bz, wacc[k]);
-    __builtin_amdgcn_wave_barrier();  // ring writes of all lanes before the tap reads
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int c = cw + (u * 4 + q) * V;
-      float acc[V];
+      float acc[V], x0[V];
+#pragma unroll
+      for (int h = 0; h < V / 4; ++h) {
+        const f32x4 x4 = xrow(tau, u)[h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x0[4 * h + e] = x4[e];
+      }
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         const int m = u * GPV + i / Gm::H;
-        acc[i] = wacc[0][m >> 2][m & 3] * x0[u][i];
+        acc[i] = wacc[0][m >> 2][m & 3] * x0[i];
       }
 #pragma unroll
       for (int k = 1; k < W; ++k) {
-        const f32x4 *src = xslot(tau - k, u);
 #pragma unroll
         for (int h = 0; h < V / 4; ++h) {
-          const f32x4 x4 = src[h];
+          const f32x4 x4 = xrow(tau - k, u)[h];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * h + e;
@@ -305,11 +323,18 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
       for (int i = 0; i < V; ++i) {
         float sv = acc[i];
         if constexpr (ACT) sv = silu_f(sv);
-        o[i] = fmaf(rho, x0[u][i], sv);
+        o[i] = fmaf(rho, x0[i], sv);
       }
-      if (valid && c < D) st16(y + (seq + tau) * D + c, pack<E>(o));
+      *reinterpret_cast<uint4 *>(stage + j * SP + (wave * Gm::CW + (u * 4 + q) * V) * (int)sizeof(E)) =
+          pack<E>(o);
     }
-    __builtin_amdgcn_wave_barrier();  // tap reads before the next tile's writes
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int r = p * RPP + rr;
+      const uint4 val = *reinterpret_cast<const uint4 *>(stage + r * SP + vv * 16);
+      if (t + r < t1 && cc_ok) st16(y + (seq + t + r) * D + cc, val);
+    }
   };
 #pragma unroll
   for (int p = 0; p < PF; ++p)

@@ -17,7 +17,7 @@ static hipError_t launch_lr_fwd(const LrArgs &a) {
   const int nchunk = (int)((a.T + TC - 1) / TC);
   const int64_t nblocks = a.B * nchunk * (int64_t)ncb;
   if (nblocks == 0) return hipSuccess;
-  constexpr int smem = LrFwdSmem<E, W, GPV>::bytes;
+  constexpr int smem = LrFwdGeo<E, W, GPV>::bytes;
   hipLaunchKernelGGL((lr_fwd_kernel<E, W, GPV, ACT>), dim3((unsigned)nblocks),
                      dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
                      (const E *)a.U, (E *)a.y, (int)a.T, (int)a.D, a.R, TC, nchunk, ncb, rho);
