@@ -67,12 +67,11 @@ inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int 
   LrBwdPlan p{};
   p.V = bf16 ? 8 : 4;
   p.gpv = p.V / H;
-  const int numax = W <= 3 ? 4 : W <= 6 ? 2 : 1;  // must match LrGeo::NU
-  p.units = H < numax ? H : numax;   // channel vectors per lane
+  p.units = 1;  // channel vectors per lane (LrGeo::NU)
   p.cb = (int64_t)4 /*waves*/ * 4 /*quarters*/ * p.units * p.V;
   p.ncb = (D + p.cb - 1) / p.cb;
   p.rpad = 16;  // R <= 16: one 16-row MFMA block of ranks
-  p.tc = pick_chunk(B, T, p.ncb, 512);  // 2 resident workgroups per CU
+  p.tc = pick_chunk(B, T, p.ncb, 768);  // 3 resident workgroups per CU
   p.nchunk = (T + p.tc - 1) / p.tc;
   const int64_t G = D / H;
   p.dz_part = (size_t)p.ncb * (size_t)(B * T) * (size_t)p.rpad * 4;

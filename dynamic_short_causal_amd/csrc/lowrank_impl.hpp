@@ -8,11 +8,12 @@
 // once; they never reach device memory.  The backward is the derivative.
 //
 // Work decomposition.  A workgroup (4 waves) owns a block of CB channels and a
-// chunk of tokens of one sequence; each wave owns CW = 4*NU*V channels.  The
-// wave walks its chunk in tiles of 16 tokens.  Inside a tile, lane (q, j)
-// (q = lane / 16, j = lane % 16) handles token t+j and the NU channel vectors
-// u*4 + q of the wave's slice, so one wave instruction touches 16 token rows
-// at 4 adjacent 16-byte vectors.
+// chunk of tokens of one sequence; each wave owns CW = 4*V channels.  The
+// workgroup walks its chunk in tiles of 16 tokens.  Device memory is touched
+// by whole rows of the channel block (consecutive threads, consecutive
+// 16-byte vectors) that go through LDS; inside a tile, lane (q, j)
+// (q = lane / 16, j = lane % 16) computes token t+j and channel vector q of
+// its wave's slice.
 //
 // Filters on chip: for every tap k the wave issues 16x16 MFMAs whose B operand
 // is z^T of 16 tokens (K = ranks) and whose A operand holds the U columns of
@@ -23,24 +24,22 @@
 // v_mfma_f32_16x16x4_f32.
 //
 // Shifted rows.  The rows of other tokens (x at t-k for the taps, ds at t+k
-// for dx) go through a 32-row LDS ring, written once per tile and read back
-// with 16-byte LDS reads, so the shifts cost LDS bandwidth rather than
-// vector-ALU issue.  The forward's ring spans the workgroup and is filled by
-// row-major loads; its outputs leave through an LDS staging tile, so every
-// device-memory access is a whole-row segment of the channel block.
+// for dx) come from 32-row fp32 LDS rings spanning the workgroup, filled once
+// per tile by the row-major loads and read back with 16-byte LDS reads.
 //
 // Backward per tile (one-tile lag for dx):
 //   * ds = dy (or dy * SiLU'(s), s recomputed from the on-chip filters);
 //   * dx[t] = rho dy[t] + sum_k w[t+k,k] ds[t+k] for the previous tile: the
-//     filters w[t+k,.,k] come from MFMAs fed with z of token t+k, ds[t+k]
+//     filters w[t+k,.,k] come from MFMAs fed with z of token t+k (without
+//     SiLU the residual is folded into the tap-0 filter: ds = dy), ds[t+k]
 //     from the ds ring; a final step over the tokens after the chunk (zero
 //     past the sequence end) completes the chunk's last tile;
 //   * dw (on chip only) -> dz^T += U dw^T with 16x16x32 bf16 MFMAs (K = the
 //     lane's slots), summed across the 4 waves in LDS and written as one fp32
 //     partial per channel block;
-//   * dU^T += dw^T z: dw is transposed through LDS so tokens become the K
-//     dimension; accumulated over the whole chunk in registers and written
-//     once per chunk as an fp32 partial.
+//   * dU^T += dw^T z: dw is transposed through LDS, one 16-row block at a
+//     time, so tokens become the K dimension; accumulated over the whole
+//     chunk in registers and written once per chunk as an fp32 partial.
 // A second kernel adds the partials in a fixed order (deterministic).
 #pragma once
 #include <type_traits>
@@ -59,9 +58,9 @@ template <typename E, int W, int GPV> struct LrGeo {
   static constexpr bool BF = sizeof(E) == 2;
   static constexpr int V = Vw<E>::n;
   static constexpr int H = V / GPV;         // channels per filter group
-  // channel vectors per lane: up to 4, fewer for wide filters (register budget)
-  static constexpr int NUMAX = W <= 3 ? 4 : W <= 6 ? 2 : 1;
-  static constexpr int NU = H < NUMAX ? H : NUMAX;
+  // one channel vector per lane: keeps the registers and LDS of the backward
+  // small enough for three resident workgroups per CU
+  static constexpr int NU = 1;
   static constexpr int NG = NU * GPV;       // (group, vector) instances per lane per tap
   static constexpr int NP = (NG + 3) / 4;   // filter MFMAs per tap (4 rows per lane each)
   static constexpr int NS = NG * W;         // filter slots per lane
@@ -349,35 +348,63 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
 // ---------------------------------------------------------------------------
 // Backward
 // ---------------------------------------------------------------------------
-template <typename E, int W, int GPV> struct LrBwdSmem {
+// Device memory is read and written through buffer resources covering one
+// 16-token slab each: rows past the sequence (or channels past D, given an
+// offset above the resource size) read as zero and are not written, so no
+// load or store needs a mask or 64-bit address arithmetic.
+typedef __amdgpu_buffer_rsrc_t brsrc;
+__device__ __forceinline__ brsrc mk_rsrc(const void *p, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
+}
+constexpr uint32_t kOOB = 0x80000000u;
+
+template <typename E, int W, int GPV> struct LrBwdGeo {
   using Gm = LrGeo<E, W, GPV>;
-  // per wave: dw^T, 4*NS slot rows x 16 tokens, padded with zero rows to
-  // whole 16-row MFMA blocks
+  static constexpr int RS = (int)sizeof(E);
+  static constexpr int XP = Gm::CB * 4 + 16;   // x ring row pitch (fp32)
+  static constexpr int DP = Gm::CB * 4 + 16;   // ds ring row pitch (fp32)
+  static constexpr int SP = Gm::CB * RS + 16;  // dx staging row pitch
+  // z ring row: 16 ranks + 8 bytes, so 16 lanes reading 16 rows hit distinct banks
+  static constexpr int ZP = 16 * RS + 8;
+  static constexpr int VPR = Gm::CB / Gm::V;
+  static constexpr int RPP = kLrThreads / VPR;
+  static constexpr int NPASS = 16 / RPP;
+  static_assert(RPP * NPASS == 16, "a slab is a whole number of passes");
   static constexpr int nrb = (Gm::NS + 3) / 4;
-  static constexpr int dwt_bytes = 16 * nrb * 16 * (int)sizeof(E);
-  static constexpr int xring_bytes = 32 * Gm::XROW;
-  static constexpr int dring_bytes = 32 * Gm::DROW;
-  static constexpr int wave_bytes = dwt_bytes + xring_bytes + dring_bytes;
-  // per workgroup: two buffers of the 4 waves' dz^T tiles (64 lanes x 4)
-  static constexpr int dz_floats = 2 * 4 * 64 * 4;
-  static constexpr int bytes = 4 * wave_bytes + dz_floats * 4;
+  static constexpr int DWP = 20;  // dw^T block row: 16 tokens + 4 (bank spread)
+  static constexpr int dwt_wave = 2 * 16 * DWP * RS;
+  static constexpr int o_x = 0;
+  static constexpr int o_ds = o_x + 32 * XP;
+  static constexpr int o_dx = o_ds + 32 * DP;
+  static constexpr int o_z = o_dx + 16 * SP;
+  static constexpr int o_dz = o_z + 32 * ZP;
+  static constexpr int o_dwt = o_dz + 4 * 64 * 16;
+  static constexpr int bytes = o_dwt + 4 * dwt_wave;
 };
 
-// Two waves per SIMD (at most 256 VGPR+AGPR per lane) where the compiler fits
-// that without spilling, one otherwise.  The set was read off the kernel
-// resource-usage report of every instance.
+template <typename E, int W, int GPV>
+__device__ __forceinline__ void gen_tap_init(
+    const typename WFrag<sizeof(E) == 2>::T (&a)[LrGeo<E, W, GPV>::NP][LrGeo<E, W, GPV>::KS],
+    const typename WFrag<sizeof(E) == 2>::T (&bz)[LrGeo<E, W, GPV>::KS],
+    f32x4 (&acc)[LrGeo<E, W, GPV>::NP], float init) {
+  using Gm = LrGeo<E, W, GPV>;
+#pragma unroll
+  for (int p = 0; p < Gm::NP; ++p) {
+    f32x4 c = {init, init, init, init};
+#pragma unroll
+    for (int ks = 0; ks < Gm::KS; ++ks) c = mma_w<Gm::BF>(a[p][ks], bz[ks], c);
+    acc[p] = c;
+  }
+}
+
+// Three waves per SIMD where the compiler fits that without spilling, fewer
+// otherwise; the set was read off the kernel resource-usage report.
 template <typename E, int W, int GPV>
 constexpr int lr_bwd_min_waves() {
-  if constexpr (sizeof(E) == 2) {
-    const bool two = (W == 1 && GPV != 2) || ((W == 2 || W == 3) && GPV == 4) ||
-                     (W == 4 && (GPV == 1 || GPV == 8)) || (W == 5 && GPV == 8) ||
-                     (W == 7 && (GPV == 1 || GPV == 2));
-    return two ? 2 : 1;
-  } else {
-    const bool two = W <= 4 || (W == 5 && (GPV == 1 || GPV == 4)) ||
-                     (W == 7 && (GPV == 1 || GPV == 2)) || (W == 8 && GPV == 1);
-    return two ? 2 : 1;
-  }
+  if constexpr (sizeof(E) == 2)
+    return GPV == 8 && W == 8 ? 1 : (GPV == 8 && W >= 5) || (GPV == 4 && W == 8) ? 2 : 3;
+  else return GPV == 4 && W >= 7 ? 2 : 3;
 }
 
 template <typename E, int W, int GPV>
@@ -387,17 +414,22 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
     float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk, int ncb, int64_t N,
     float rho, int act) {
   using Gm = LrGeo<E, W, GPV>;
-  using Sm = LrBwdSmem<E, W, GPV>;
+  using Bg = LrBwdGeo<E, W, GPV>;
   constexpr bool BF = Gm::BF;
   constexpr int V = Gm::V, NU = Gm::NU, NG = Gm::NG, NP = Gm::NP, NS = Gm::NS, KS = Gm::KS;
-  constexpr int NDZ = BF ? (NS + 7) / 8 : NS;  // dz MFMAs per tile
-  constexpr int NRB = Sm::nrb;                 // 16-row blocks of the wave's 4*NS slots
-  constexpr int RP = 16;
-  constexpr int XROW = Gm::XROW, DROW = Gm::DROW;
-  const bool ACT = act != 0;  // wave-uniform
+  constexpr int NDZ = BF ? (NS + 7) / 8 : NS;
+  constexpr int NRB = Bg::nrb;
+  constexpr int RP = 16, RS = Bg::RS;
+  constexpr int XP = Bg::XP, DP = Bg::DP, SP = Bg::SP, ZP = Bg::ZP, VPR = Bg::VPR, RPP = Bg::RPP,
+                NPASS = Bg::NPASS;
+  constexpr int PF = 1;  // loads one step ahead: a step outlasts the load latency
+  const bool ACT = act != 0;
   extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char *xring = smem + Bg::o_x, *dring = smem + Bg::o_ds, *dxstage = smem + Bg::o_dx,
+                *zring = smem + Bg::o_z;
+  float *dzbuf = reinterpret_cast<float *>(smem + Bg::o_dz);
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, j = lane & 15;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, j = lane & 15;
   int bid = blockIdx.x;
   const int cb = bid % ncb;
   bid /= ncb;
@@ -407,23 +439,44 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
   const int t0 = chunk * TC, t1 = min(T, t0 + TC);
   const int GW = (D / Gm::H) * W;
   const int64_t seq = (int64_t)b * T;
+  E *dwt = reinterpret_cast<E *>(smem + Bg::o_dwt + wave * Bg::dwt_wave);
 
-  unsigned char *wbase = smem + wave * Sm::wave_bytes;
-  E *dwt = reinterpret_cast<E *>(wbase);
-  unsigned char *xring = wbase + Sm::dwt_bytes;
-  unsigned char *dring = xring + Sm::xring_bytes;
-  float *dzbuf = reinterpret_cast<float *>(smem + 4 * Sm::wave_bytes);
+  // row-major role: vector vv of rows rr + p*RPP; byte offsets inside a 16-row slab
+  const int vv = tid % VPR, rr = tid / VPR;
+  const int cc = cb * Gm::CB + vv * V;
+  const uint32_t cbase = cc < D ? (uint32_t)cc * RS : kOOB;
+  uint32_t voff[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) voff[p] = cbase + (uint32_t)((p * RPP + rr) * D * RS);
+  const int lcol = wave * Gm::CW;
   auto xslot = [&](int tok, int u) {
-    return reinterpret_cast<uint4 *>(xring + (tok & 31) * XROW + (u * 4 + q) * 16);
+    return reinterpret_cast<const f32x4 *>(xring + (tok & 31) * XP + (lcol + (u * 4 + q) * V) * 4);
   };
-  // ds ring: V fp32 of vector u at token tok, as V/4 16-byte pieces
   auto dslot = [&](int tok, int u) {
-    return reinterpret_cast<f32x4 *>(dring + (tok & 31) * DROW + (u * 4 + q) * V * 4);
+    return reinterpret_cast<f32x4 *>(dring + (tok & 31) * DP + (lcol + (u * 4 + q) * V) * 4);
   };
-  // rows 4*NS .. 16*NRB-1 pad the last dw^T MFMA block and stay zero
-  for (int r = 4 * NS + (lane >> 4); r < 16 * NRB; r += 4) dwt[r * 16 + (lane & 15)] = (E)0;
+  auto zrow = [&](int tok) { return reinterpret_cast<const E *>(zring + (tok & 31) * ZP); };
+  auto zfrag = [&](int tok, typename WFrag<BF>::T (&f)[KS]) {
+    const E *zr = zrow(tok);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (BF) f[ks] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(zr + 4 * q));
+      else f[ks] = zr[ks * 4 + q];
+    }
+  };
+  // 16-token slab resources: rows t .. t+15 of a [B*T, D] tensor, bounded by `lim`
+  auto slab = [&](const E *base, int t, int lim) {
+    return mk_rsrc(base + (seq + t) * (int64_t)D, (int64_t)(min(lim, t + 16) - t) * D * RS);
+  };
+  const bool z_on = tid < 16 * R;
+  const uint32_t zoff = z_on ? (uint32_t)tid * RS : kOOB;
+  const int zr_tok = tid / (R > 0 ? R : 1), zr_rank = tid - zr_tok * (R > 0 ? R : 1);
+  auto zslab = [&](int t, int lim) {
+    return mk_rsrc(z + (seq + t) * (int64_t)R, (int64_t)(min(lim, t + 16) - t) * R * RS);
+  };
 
-  // resident operands: filter A fragments and dz A fragments (U columns)
+  for (int i = tid; i < 32 * ZP / 4; i += kLrThreads) reinterpret_cast<uint32_t *>(zring)[i] = 0u;
+
   typename WFrag<BF>::T aw[W][NP][KS];
   load_wA<E, W, GPV>(U, GW, R, cw, D, lane, aw);
   typename DzFrag<BF>::T adz[NDZ];
@@ -448,161 +501,147 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
       }
     }
   }
-
   f32x4 accU[NRB];
 #pragma unroll
   for (int a = 0; a < NRB; ++a) accU[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // x rows of the 16 tokens before the chunk (zero before the sequence start)
+  const int tiles = (t1 - t0 + 15) / 16;
+  const int nsteps = tiles + 1;
+  __syncthreads();  // z ring zeroed
+  // prologue: x and z of the 16 tokens before the chunk (none before the sequence)
+  {
+    const int tb = t0 - 16;
+    const brsrc rx = slab(x, tb, tb < 0 ? tb : T);
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int c = cw + (u * 4 + q) * V;
-    const int tb = t0 - 16 + j;
-    const bool ok = tb >= 0 && c < D;
-    *xslot(tb, u) = sel4(ok, ld16(x + (ok ? (seq + tb) * D + c : 0)));
+    for (int p = 0; p < NPASS; ++p) {
+      const uint4 raw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff[p], 0, 0));
+      float v[V];
+      unpack<E>(raw, v);
+      f32x4 *dst = reinterpret_cast<f32x4 *>(xring + ((tb + p * RPP + rr) & 31) * XP + vv * V * 4);
+#pragma unroll
+      for (int h = 0; h < V / 4; ++h) dst[h] = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+    }
+    const brsrc rz = zslab(tb, tb < 0 ? tb : T);
+    if (z_on) {
+      E v;
+      if constexpr (BF) v = (E)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
+      else v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, 0, 0));
+      reinterpret_cast<E *>(zring + ((tb + zr_tok) & 31) * ZP)[zr_rank] = v;
+    }
   }
 
-  // Loads of one step, issued a step ahead and branch-free: a lane without a
-  // token (past T) or a channel (past D) reads row 0 instead, and the value is
-  // zeroed where it is used.
-  typedef typename WFrag<BF>::T wfrag_t;
-  typedef typename std::conditional<BF, short, float>::type zt_t;
-  wfrag_t zn[KS];        // z of the step's own tokens (SiLU only)
-  wfrag_t zsn[W][KS];    // z of tokens t-16+j+k: filters w[t'+k, ., k] for dx
-  uint4 dyn[NU], xn[NU];
-  zt_t ztn[4];           // z[t + 4qa + e][n]: the dU B operand (K = tokens);
-                         // rows past the chunk meet zero dw rows, ranks n >= R
-                         // give dU rows that are never read: no masking
-  const int tiles = (t1 - t0 + 15) / 16;
-  const int nsteps = tiles + 1;  // + the tokens after the chunk (dx of its last tile)
-  // per-lane element offsets of the first tile's row, advanced by 16 rows a step
-  int64_t row0[NU];
-  bool chan_ok[NU];
+  uint4 xn[PF][NPASS], dyn[PF][NPASS];
+  E zn[PF];
+  auto issue = [&](int st, int sl) {
+    const int t = t0 + 16 * st;
+    const bool halo = st == tiles;
+    const brsrc rdy = slab(dy, t, T);
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int c = cw + (u * 4 + q) * V;
-    chan_ok[u] = c < D;
-    row0[u] = (seq + t0 + j) * D + c;
-  }
-  auto issue = [&](int st) {
+    for (int p = 0; p < NPASS; ++p)
+      dyn[sl][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rdy, voff[p], 0, 0));
+    if (ACT || !halo) {
+      const brsrc rx = slab(x, t, T);
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p)
+        xn[sl][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff[p], 0, 0));
+    }
+    const brsrc rz = zslab(t, T);
+    if constexpr (BF) zn[sl] = (E)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
+    else zn[sl] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, 0, 0));
+  };
+  auto fill = [&](int st, int sl) {
+    const int t = t0 + 16 * st;
+    const bool halo = st == tiles;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int row = (t + p * RPP + rr) & 31;
+      float v[V];
+      unpack<E>(dyn[sl][p], v);
+      f32x4 *dd = reinterpret_cast<f32x4 *>(dring + row * DP + vv * V * 4);
+#pragma unroll
+      for (int h = 0; h < V / 4; ++h) dd[h] = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+      if (ACT || !halo) {
+        float w[V];
+        unpack<E>(xn[sl][p], w);
+        f32x4 *xd = reinterpret_cast<f32x4 *>(xring + row * XP + vv * V * 4);
+#pragma unroll
+        for (int h = 0; h < V / 4; ++h) xd[h] = f32x4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
+      }
+    }
+    if (z_on) reinterpret_cast<E *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn[sl];
+  };
+
+  float dyp[NU][V];  // (SiLU only) dy of the previous tile, for the residual term of its dx
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int i = 0; i < V; ++i) dyp[u][i] = 0.f;
+  const float rho_act = ACT ? rho : 0.f;   // residual through dy (SiLU)
+  const float rho_tap = ACT ? 0.f : rho;   // residual folded into the tap-0 filter (ds = dy)
+  auto step = [&](int st, int sl) {
     const int t = t0 + 16 * st;
     const bool halo = st == tiles;
     const int tau = t + j;
-    const bool in_seq = tau < T;
-    if (ACT) load_zB<E, KS>(z, seq + tau, in_seq, R, q, zn);
-    if (st > 0) {
+    fill(st, sl);
+    if (st + PF < nsteps) issue(st + PF, sl);
+    __syncthreads();  // (1) rings and slabs of this step written
+    float dxa[NU][V];
 #pragma unroll
-      for (int k = 0; k < W; ++k) {
-        const int tk = t - 16 + j + k;
-        load_zB<E, KS>(z, seq + tk, tk < T, R, q, zsn[k]);
-      }
-    }
-    const int64_t step_off = (int64_t)(16 * st) * D;
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int64_t off = in_seq && chan_ok[u] ? row0[u] + step_off : 0;
-      dyn[u] = ld16(dy + off);
-      if (ACT || !halo) xn[u] = ld16(x + off);
-    }
-    if (!halo) {
-      const int qa = lane >> 4, n = lane & 15;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int tk = BF ? t + 4 * qa + e2 : t + 4 * e2 + qa;
-        const bool ok = tk < t1 && n < R;
-        if constexpr (BF) ztn[e2] = (short)z[ok ? (seq + tk) * R + n : 0];
-        else ztn[e2] = z[ok ? (seq + tk) * R + n : 0];
-      }
-    }
-  };
-  issue(0);
-
-  float dyp[NU][V];  // dy of the previous tile (residual term of its dx)
-  int parity = 0;
-  for (int st = 0; st < nsteps; ++st) {
-    const int t = t0 + 16 * st;
-    const bool halo = st == tiles;  // wave-uniform
-    const int tau = t + j;
-    const bool in_seq = tau < T;
-
-    wfrag_t bz[KS], bzs[W][KS];
-    uint4 dyr[NU], xc[NU];
-    zt_t zt[4];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bz[ks] = zn[ks];
-#pragma unroll
-    for (int k = 0; k < W; ++k)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) bzs[k][ks] = zsn[k][ks];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const bool act_lane = in_seq && cw + (u * 4 + q) * V < D;
-      dyr[u] = sel4(act_lane, dyn[u]);
-      xc[u] = sel4(act_lane && (ACT || !halo), xn[u]);
-    }
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) zt[e2] = ztn[e2];
-    if (st + 1 < nsteps) issue(st + 1);
-
-    // own x row into the ring (taps of later tokens)
-    if (ACT || !halo) {
-#pragma unroll
-      for (int u = 0; u < NU; ++u) *xslot(tau, u) = xc[u];
-    }
-    __builtin_amdgcn_wave_barrier();
-    // x tap k of vector u for this lane's token (zero before the sequence)
-    auto xtap = [&](int u, int k, float (&o)[V]) {
-      unpack<E>(k == 0 ? xc[u] : *xslot(tau - k, u), o);
-    };
-
-    // ds = dy (or dy * SiLU'(s)) of this tile's tokens, into the ds ring
+      for (int i = 0; i < V; ++i) dxa[u][i] = rho_act * dyp[u][i];
+    // own ds (= dy, or dy * SiLU'(s))
     float ds[NU][V];
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int h = 0; h < V / 4; ++h) {
+        const f32x4 d4 = dslot(tau, u)[h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ds[u][4 * h + e] = d4[e];
+      }
     if (ACT) {
+      typename WFrag<BF>::T bz[KS];
+      zfrag(tau, bz);
       f32x4 wacc[W][NP];
 #pragma unroll
       for (int k = 0; k < W; ++k) gen_tap<E, W, GPV>(aw[k], bz, wacc[k]);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        float sacc[V], dyv[V];
-        unpack<E>(dyr[u], dyv);
+        float sacc[V];
 #pragma unroll
         for (int i = 0; i < V; ++i) sacc[i] = 0.f;
 #pragma unroll
-        for (int k = 0; k < W; ++k) {
-          float xk[V];
-          xtap(u, k, xk);
+        for (int k = 0; k < W; ++k)
 #pragma unroll
-          for (int i = 0; i < V; ++i) {
-            const int m = u * GPV + i / Gm::H;
-            sacc[i] = fmaf(wacc[k][m >> 2][m & 3], xk[i], sacc[i]);
+          for (int h = 0; h < V / 4; ++h) {
+            const f32x4 x4 = xslot(tau - k, u)[h];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * h + e, m = u * GPV + i / Gm::H;
+              sacc[i] = fmaf(wacc[k][m >> 2][m & 3], x4[e], sacc[i]);
+            }
           }
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          dyp[u][i] = ds[u][i];
+          ds[u][i] = ds[u][i] * silu_grad_f(sacc[i]);
         }
 #pragma unroll
-        for (int i = 0; i < V; ++i) ds[u][i] = dyv[i] * silu_grad_f(sacc[i]);
+        for (int h = 0; h < V / 4; ++h)
+          dslot(tau, u)[h] = f32x4{ds[u][4 * h], ds[u][4 * h + 1], ds[u][4 * h + 2], ds[u][4 * h + 3]};
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < NU; ++u) unpack<E>(dyr[u], ds[u]);  // ds = dy
     }
-#pragma unroll
-    for (int u = 0; u < NU; ++u)
-#pragma unroll
-      for (int h = 0; h < V / 4; ++h)
-        dslot(tau, u)[h] = f32x4{ds[u][4 * h], ds[u][4 * h + 1], ds[u][4 * h + 2], ds[u][4 * h + 3]};
     __builtin_amdgcn_wave_barrier();
-
     // dx of the previous tile: dx[t'] = rho dy[t'] + sum_k w[t'+k,.,k] ds[t'+k]
     if (st > 0) {
       const int tp = t - 16 + j;
-      float dxa[NU][V];
-#pragma unroll
-      for (int u = 0; u < NU; ++u)
-#pragma unroll
-        for (int i = 0; i < V; ++i) dxa[u][i] = rho * dyp[u][i];
 #pragma unroll
       for (int k = 0; k < W; ++k) {
+        typename WFrag<BF>::T bzs[KS];
+        zfrag(tp + k, bzs);
         f32x4 wk[NP];
-        gen_tap<E, W, GPV>(aw[k], bzs[k], wk);
+        gen_tap_init<E, W, GPV>(aw[k], bzs, wk, k == 0 ? rho_tap : 0.f);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
           const f32x4 *src = dslot(tp + k, u);
@@ -611,137 +650,134 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
             const f32x4 d4 = src[h];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int i = 4 * h + e;
-              const int m = u * GPV + i / Gm::H;
+              const int i = 4 * h + e, m = u * GPV + i / Gm::H;
               dxa[u][i] = fmaf(wk[m >> 2][m & 3], d4[e], dxa[u][i]);
             }
           }
         }
       }
-      if (tp < t1) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int c = cw + (u * 4 + q) * V;
-          if (c < D) st16(dx + (seq + tp) * D + c, pack<E>(dxa[u]));
-        }
-      }
+      for (int u = 0; u < NU; ++u)
+        *reinterpret_cast<uint4 *>(dxstage + j * SP + (lcol + (u * 4 + q) * V) * RS) = pack<E>(dxa[u]);
     }
-    if (ACT) {
-#pragma unroll
-      for (int u = 0; u < NU; ++u) unpack<E>(dyr[u], dyp[u]);
-    } else {
+    if (!halo) {
+      // filter-gradient slots; a chunk ends inside a tile only at the sequence
+      // end, where ds is zero, so no lane needs masking
+      float dwv[NS];
 #pragma unroll
       for (int u = 0; u < NU; ++u)
 #pragma unroll
-        for (int i = 0; i < V; ++i) dyp[u][i] = ds[u][i];
-    }
-    if (halo) break;
-
-    // filter gradient slots of this tile.  A chunk ends inside a tile only at
-    // the sequence end, where ds is already zero, so no lane needs masking.
-    float dwv[NS];
+        for (int k = 0; k < W; ++k) {
+          float xk[V];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
+          for (int h = 0; h < V / 4; ++h) {
+            const f32x4 x4 = xslot(tau - k, u)[h];
 #pragma unroll
-      for (int k = 0; k < W; ++k) {
-        float xk[V];
-        xtap(u, k, xk);
+            for (int e = 0; e < 4; ++e) xk[4 * h + e] = x4[e];
+          }
 #pragma unroll
-        for (int gi = 0; gi < GPV; ++gi) {
-          float a = 0.f;
+          for (int gi = 0; gi < GPV; ++gi) {
+            float a = 0.f;
 #pragma unroll
-          for (int h = 0; h < Gm::H; ++h)
-            a = fmaf(ds[u][gi * Gm::H + h], xk[gi * Gm::H + h], a);
-          dwv[k * NG + u * GPV + gi] = a;
-        }
-      }
-    }
-
-    // dw as bf16 pairs (slots 2i, 2i+1), rounded once, used by both MFMAs
-    constexpr int NPAIR = (NS + 1) / 2;
-    uint32_t dwp[BF ? NPAIR : 1];
-    if constexpr (BF) {
-#pragma unroll
-      for (int i = 0; i < NPAIR; ++i)
-        dwp[i] = pack_bf16x2(dwv[2 * i], 2 * i + 1 < NS ? dwv[2 * i + 1] : 0.f);
-    }
-    // ---- dz^T (16 ranks x 16 tokens) over this wave's slots ----
-    f32x4 dzacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NDZ; ++s) {
-      typename DzFrag<BF>::T bdw;
-      if constexpr (BF) {
-        uint4 v;
-        v.x = 4 * s + 0 < NPAIR ? dwp[4 * s + 0] : 0u;
-        v.y = 4 * s + 1 < NPAIR ? dwp[4 * s + 1] : 0u;
-        v.z = 4 * s + 2 < NPAIR ? dwp[4 * s + 2] : 0u;
-        v.w = 4 * s + 3 < NPAIR ? dwp[4 * s + 3] : 0u;
-        bdw = __builtin_bit_cast(bf16x8_t, v);
-      } else {
-        bdw = dwv[s];
-      }
-      dzacc = mma_dz<BF>(adz[s], bdw, dzacc);
-    }
-    // sum the 4 waves' partials in a fixed order (LDS, double-buffered)
-    float *zb = dzbuf + parity * (4 * 64 * 4);
-    *reinterpret_cast<f32x4 *>(zb + (wave * 64 + lane) * 4) = dzacc;
-    __syncthreads();
-    if (wave == 0 && tau < t1) {
-      f32x4 s4 = *reinterpret_cast<const f32x4 *>(zb + lane * 4);
-#pragma unroll
-      for (int w2 = 1; w2 < 4; ++w2) s4 += *reinterpret_cast<const f32x4 *>(zb + (w2 * 64 + lane) * 4);
-      // lane (q, j) holds ranks 4q .. 4q+3 of token tau
-      *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + tau) * RP + 4 * q) = s4;
-    }
-    parity ^= 1;
-
-    // ---- dU^T += dw^T z: transpose dw through LDS (row = slot*4 + quarter) ----
-#pragma unroll
-    for (int sg = 0; sg < NS; ++sg) {
-      if constexpr (BF) {
-        const uint32_t pr = dwp[sg >> 1];
-        dwt[(sg * 4 + q) * 16 + j] = (uint16_t)((sg & 1) ? (pr >> 16) : (pr & 0xffffu));
-      } else {
-        dwt[(sg * 4 + q) * 16 + j] = dwv[sg];
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    {
-      const int qa = lane >> 4, n = lane & 15;
-      if constexpr (BF) {
-        s16x4 bzt;
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) bzt[e2] = zt[e2];
-#pragma unroll
-        for (int a = 0; a < NRB; ++a) {
-          const uint2 v = *reinterpret_cast<const uint2 *>(dwt + (16 * a + n) * 16 + 4 * qa);
-          s16x4 af;
-          af[0] = (short)(v.x & 0xffff); af[1] = (short)(v.x >> 16);
-          af[2] = (short)(v.y & 0xffff); af[3] = (short)(v.y >> 16);
-          accU[a] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(af, bzt, accU[a], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-#pragma unroll
-          for (int a = 0; a < NRB; ++a) {
-            const float af = dwt[(16 * a + n) * 16 + 4 * s4 + qa];
-            accU[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(af, zt[s4], accU[a], 0, 0, 0);
+            for (int h = 0; h < Gm::H; ++h) a = fmaf(ds[u][gi * Gm::H + h], xk[gi * Gm::H + h], a);
+            dwv[k * NG + u * GPV + gi] = a;
           }
         }
+      constexpr int NPAIR = (NS + 1) / 2;
+      uint32_t dwp[BF ? NPAIR : 1];
+      if constexpr (BF) {
+#pragma unroll
+        for (int i = 0; i < NPAIR; ++i)
+          dwp[i] = pack_bf16x2(dwv[2 * i], 2 * i + 1 < NS ? dwv[2 * i + 1] : 0.f);
+      }
+      f32x4 dzacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < NDZ; ++s2) {
+        typename DzFrag<BF>::T bdw;
+        if constexpr (BF) {
+          uint4 v;
+          v.x = 4 * s2 + 0 < NPAIR ? dwp[4 * s2 + 0] : 0u;
+          v.y = 4 * s2 + 1 < NPAIR ? dwp[4 * s2 + 1] : 0u;
+          v.z = 4 * s2 + 2 < NPAIR ? dwp[4 * s2 + 2] : 0u;
+          v.w = 4 * s2 + 3 < NPAIR ? dwp[4 * s2 + 3] : 0u;
+          bdw = __builtin_bit_cast(bf16x8_t, v);
+        } else {
+          bdw = dwv[s2];
+        }
+        dzacc = mma_dz<BF>(adz[s2], bdw, dzacc);
+      }
+      *reinterpret_cast<f32x4 *>(dzbuf + (wave * 64 + lane) * 4) = dzacc;
+      // dU^T += dw^T z, one 16-row block (slots 4a..4a+3 of every quarter) at a time
+      const int qa = lane >> 4, n = lane & 15;
+      typename WFrag<BF>::T bzt[KS];
+      if constexpr (BF) {
+        s16x4 f;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) f[e2] = (short)zrow(t + 4 * qa + e2)[n];
+        bzt[0] = f;
+      } else {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) bzt[s4] = zrow(t + 4 * s4 + qa)[n];
+      }
+#pragma unroll
+      for (int a = 0; a < NRB; ++a) {
+        E *blk = dwt + (a & 1) * 256;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sg = 4 * a + e;
+          E v = (E)0;
+          if (sg < NS) {
+            if constexpr (BF) {
+              const uint32_t pr = dwp[sg >> 1];
+              v = (uint16_t)((sg & 1) ? (pr >> 16) : (pr & 0xffffu));
+            } else {
+              v = dwv[sg];
+            }
+          }
+          blk[(e * 4 + q) * 16 + j] = v;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if constexpr (BF) {
+          const uint2 v = *reinterpret_cast<const uint2 *>(blk + n * 16 + 4 * qa);
+          accU[a] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v), bzt[0], accU[a], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4)
+            accU[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(blk[n * 16 + 4 * s4 + qa], bzt[s4], accU[a], 0, 0, 0);
+        }
       }
     }
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();  // (2) dx staging and dz partials complete; ring reads done
+    if (st > 0) {
+      const brsrc rdx = slab(dx, t - 16, t1);
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const uint4 val = *reinterpret_cast<const uint4 *>(dxstage + (p * RPP + rr) * SP + vv * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, val), rdx, voff[p], 0, 0);
+      }
+    }
+    if (!halo && wave == 0 && tau < t1) {
+      f32x4 s4 = *reinterpret_cast<const f32x4 *>(dzbuf + lane * 4);
+#pragma unroll
+      for (int w2 = 1; w2 < 4; ++w2) s4 += *reinterpret_cast<const f32x4 *>(dzbuf + (w2 * 64 + lane) * 4);
+      *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + tau) * RP + 4 * q) = s4;
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < nsteps) issue(p, p);
+  for (int st = 0; st < nsteps; st += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (st + p < nsteps) step(st + p, p);
   }
-  // dU partial of this chunk: lane (qo, n) holds rows 16a + 4qo + e
-  // = (slot 4a + qo, quarter e) for rank n
   {
     const int qo = lane >> 4, n = lane & 15;
     float *dst = dUp + (int64_t)(b * nchunk + chunk) * RP * GW;
 #pragma unroll
     for (int a = 0; a < NRB; ++a) {
       const int sg = 4 * a + qo;
-      if (sg >= NS) continue;  // padding rows of the last block
+      if (sg >= NS) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int col = slot_col<E, W, GPV>(cw, e, sg / NG, sg % NG, D);
@@ -752,40 +788,45 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
   }
 }
 
-// ---------------------------------------------------------------------------
-// Deterministic reduction of the partials: dz = sum over channel blocks,
-// dU = sum over chunks, each in ascending block order, then cast.
-// ---------------------------------------------------------------------------
+// partial sums in a fixed order, loads issued 8 at a time
 template <typename E>
 __global__ __launch_bounds__(256) void lr_reduce_kernel(const float *__restrict__ dzp,
-                                                        const float *__restrict__ dUp,
-                                                        E *__restrict__ dz, E *__restrict__ dU,
-                                                        int64_t N, int R, int RP, int ncb,
-                                                        int64_t GW, int nparts) {
+                                                         const float *__restrict__ dUp,
+                                                         E *__restrict__ dz, E *__restrict__ dU,
+                                                         int64_t N, int R, int RP, int ncb,
+                                                         int64_t GW, int nparts) {
   const int64_t nz = N * R, nu = (int64_t)R * GW;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nz + nu;
        idx += (int64_t)gridDim.x * blockDim.x) {
-    float acc = 0.f;
+    const float *src;
+    int64_t stride;
+    int cnt;
     if (idx < nz) {
       const int64_t n = idx / R;
-      const int r = (int)(idx % R);
-      for (int c = 0; c < ncb; ++c) acc += dzp[((int64_t)c * N + n) * RP + r];
-      if constexpr (sizeof(E) == 2) {
-        dz[idx] = __builtin_bit_cast(uint16_t, (__bf16)acc);
-      } else {
-        dz[idx] = acc;
-      }
+      const int r = (int)(idx - n * R);
+      src = dzp + n * RP + r; stride = N * RP; cnt = ncb;
     } else {
       const int64_t o = idx - nz;
-      const int64_t r = o / GW, col = o % GW;
-      for (int c = 0; c < nparts; ++c) acc += dUp[((int64_t)c * RP + r) * GW + col];
-      if constexpr (sizeof(E) == 2) {
-        dU[o] = __builtin_bit_cast(uint16_t, (__bf16)acc);
-      } else {
-        dU[o] = acc;
-      }
+      const int64_t r = o / GW, col = o - r * GW;
+      src = dUp + r * GW + col; stride = (int64_t)RP * GW; cnt = nparts;
+    }
+    float acc = 0.f;
+    int c = 0;
+    for (; c + 8 <= cnt; c += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = src[(c + i) * stride];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += v[i];
+    }
+    for (; c < cnt; ++c) acc += src[c * stride];
+    if constexpr (sizeof(E) == 2) {
+      if (idx < nz) dz[idx] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+      else dU[idx - nz] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+    } else {
+      if (idx < nz) dz[idx] = acc;
+      else dU[idx - nz] = acc;
     }
   }
 }
-
 }  // namespace dsc

@@ -35,9 +35,9 @@ static hipError_t launch_lr_bwd(const LrArgs &a) {
   float *dUp = (float *)((char *)a.ws + p.dz_part);
   const int64_t nblocks = a.B * p.nchunk * p.ncb;
   if (nblocks > 0) {
-    using Sm = LrBwdSmem<E, W, GPV>;
+    constexpr int smem = LrBwdGeo<E, W, GPV>::bytes;
     hipLaunchKernelGGL((lr_bwd_kernel<E, W, GPV>), dim3((unsigned)nblocks),
-                       dim3(kLrThreads), Sm::bytes, s, (const E *)a.x, (const E *)a.z,
+                       dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
                        (const E *)a.U, (const E *)a.dy, (E *)a.dx, dzp, dUp, (int)a.T, (int)a.D,
                        a.R, p.tc, (int)p.nchunk, (int)p.ncb, N, rho, a.act ? 1 : 0);
     hipError_t e = hipGetLastError();
