@@ -79,38 +79,120 @@ def traffic_from_profiles(kernel):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(target_s=15.0):
-    """The fp64 oracle on a bounded sample: one sequence of the benchmark
-    workload, head-wise and low-rank forward + backward."""
-    import numpy as np
+def cpu_baseline(target_s=12.0):
+    """The fp64 oracle on a bounded sample of the benchmark workload: whole
+    sequences of T=2048 tokens (head-wise and low-rank forward + backward, the
+    same ops as one step), taken one after another until about target_s of
+    CPU time has passed or every sequence of the batch is done."""
     import torch
     import dsc_inputs as di
     import oracle
     orc = oracle.default()
-    D, W, Hh, R = WORKLOAD["D"], WORKLOAD["W"], WORKLOAD["H_headwise"], WORKLOAD["R"]
+    B, T, D, W = WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"]
+    Hh, R = WORKLOAD["H_headwise"], WORKLOAD["R"]
 
-    def run(T):
-        g = lambda shape, std, seed: di.randn(shape, std, seed, "bf16").to(torch.float64).numpy()
-        x = g((1, T, D), 1.0, 90000)
-        dy = g((1, T, D), 1.0, 90004)
-        w = g((1, T, D // Hh, W), 0.5, 90001)
-        z = g((1, T, R), 1.0, 90002)
-        U = g((R, D * W), (1.0 / (R * W)) ** 0.5, 90003)
+    def seq(b):
+        g = lambda shape, std, k: di.randn(shape, std, 90000 + 10 * b + k, "bf16").to(
+            torch.float64).numpy()
+        return (g((1, T, D), 1.0, 0), g((1, T, D), 1.0, 4), g((1, T, D // Hh, W), 0.5, 1),
+                g((1, T, R), 1.0, 2), g((R, D * W), (1.0 / (R * W)) ** 0.5, 3))
+
+    done, el = 0, 0.0
+    while done < B and (done == 0 or el < target_s):
+        x, dy, w, z, U = seq(done)
         t0 = time.perf_counter()
         orc.headwise_fwd(x, w, Hh, residual=True)
         orc.headwise_bwd(x, w, dy, Hh, residual=True)
         orc.lowrank_fwd(x, z, U, W, 1, residual=True)
         orc.lowrank_bwd(x, z, U, dy, W, 1, residual=True)
-        return time.perf_counter() - t0
-
-    t_small = run(32)
-    T = int(max(32, min(2048, 32 * target_s / max(t_small, 1e-3))))
-    T = max(32, (T // 32) * 32)
-    el = run(T)
-    return {"value": T / el, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
-            "sample": f"1 sequence x {T} tokens of the D=6144 W=4 batch (head-wise H=16 and "
-                      f"low-rank R=16 H=1, residual, fwd+bwd), fp64 C oracle with OpenMP; "
+        el += time.perf_counter() - t0
+        done += 1
+    return {"value": round(done * T / el, 1), "unit": "tokens/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of the {B} sequences (T={T}, D={D}, W={W}; head-wise H={Hh} and "
+                      f"low-rank R={R} H=1, residual, fwd+bwd), fp64 C oracle with OpenMP; "
                       f"{el:.1f} s"}
+
+
+OP_KERNELS = {  # op -> kernel names (rocprofv3) that one call launches
+    "headwise_fwd": ["hw_fwd_kernel"],
+    "headwise_bwd": ["hw_bwd_kernel"],
+    "lowrank_fwd": ["lr_fwd_kernel"],
+    "lowrank_bwd": ["lr_bwd_kernel", "lr_reduce_kernel"],
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"  # the 512 MiB device copy of --profile-ops
+COPY_KIB = 524288
+
+
+def summarize_profiles(d, calls):
+    """Turn the rocprofv3 outputs of the three profiling runs under `d`
+    (trace/: --kernel-trace --stats; fetch/: --pmc FETCH_SIZE; write/: --pmc
+    WRITE_SIZE, each of `python3 bench.py --profile-ops <calls>`) into
+    profiles/qkv_kernels.md and one profiles/<op>_qkv_traffic.json per op."""
+    import csv
+    import collections
+
+    def kname(n):
+        for k in sorted({k for ks in OP_KERNELS.values() for k in ks} | {COPY_KERNEL},
+                        key=len, reverse=True):
+            if k in n:
+                return k
+        return None
+
+    stats = {}
+    for row in csv.DictReader(open(os.path.join(d, "trace", "run_kernel_stats.csv"))):
+        k = kname(row["Name"])
+        if k:
+            stats[k] = (int(row["Calls"]), float(row["AverageNs"]) / 1e3)
+
+    def counter(sub, name):
+        per = collections.defaultdict(dict)
+        for row in csv.DictReader(open(os.path.join(d, sub, "run_counter_collection.csv"))):
+            k = kname(row["Kernel_Name"])
+            if k and row["Counter_Name"] == name:
+                di_ = int(row["Dispatch_Id"])
+                per[k][di_] = per[k].get(di_, 0.0) + float(row["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+    fetch, write = counter("fetch", "FETCH_SIZE"), counter("write", "WRITE_SIZE")
+    ff, wf = COPY_KIB / fetch[COPY_KERNEL], COPY_KIB / write[COPY_KERNEL]
+    B, T, D, W = WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"]
+    alg = algorithmic_bytes(B, T, D, W, WORKLOAD["H_headwise"], WORKLOAD["R"],
+                            WORKLOAD["H_lowrank"])
+    cmd = ("rocprofv3 {opt} --output-format csv -d <out>/{sub} -o run -- "
+           f"python3 bench.py --profile-ops {calls}")
+    lines = ["# Kernels of one benchmark step, B=8 T=2048 D=6144 W=4 bf16 (residual)", "",
+             "Commands (repository root, MI355X, TMPDIR=/tmp), then the summary:", ""]
+    for opt, sub in (("--kernel-trace --stats", "trace"), ("--pmc FETCH_SIZE", "fetch"),
+                     ("--pmc WRITE_SIZE", "write")):
+        lines.append("    " + cmd.format(opt=opt, sub=sub))
+    lines += [f"    python3 bench.py --summarize-profiles <out> --profile-ops {calls}", "",
+              f"Calibration: the {COPY_KIB // 1024} MiB device copy ({COPY_KERNEL}) reads "
+              f"FETCH_SIZE {fetch[COPY_KERNEL]:.0f} KiB and writes WRITE_SIZE "
+              f"{write[COPY_KERNEL]:.0f} KiB per call, so HBM bytes = {ff:.3f} x FETCH_SIZE "
+              f"+ {wf:.3f} x WRITE_SIZE (KiB).", "",
+              "| op | kernel | calls | avg us | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB |",
+              "|---|---|---|---|---|---|---|"]
+    for op, ks in OP_KERNELS.items():
+        tot = 0.0
+        for k in ks:
+            n, us = stats.get(k, (0, float("nan")))
+            hb = (ff * fetch.get(k, 0.0) + wf * write.get(k, 0.0)) * 1024
+            tot += hb
+            lines.append(f"| {op} | {k} | {n} | {us:.1f} | {fetch.get(k, 0):.0f} | "
+                         f"{write.get(k, 0):.0f} | {hb / 1e6:.1f} |")
+        op_us = sum(stats.get(k, (0, 0.0))[1] for k in ks)
+        lines.append(f"| {op} | (op total) | | {op_us:.1f} | | | {tot / 1e6:.1f} "
+                     f"(algorithmic {alg[op] / 1e6:.1f}) |")
+        with open(os.path.join(ROOT, "profiles", f"{op}_qkv_traffic.json"), "w") as f:
+            json.dump({"op": op, "kernels": ks, "hbm_bytes_per_launch": round(tot),
+                       "algorithmic_bytes": alg[op], "avg_us": round(op_us, 2),
+                       "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+                       "src_digest": src_digest(KERNEL_SOURCES[op])}, f, indent=1)
+            f.write("\n")
+    with open(os.path.join(ROOT, "profiles", "qkv_kernels.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -121,7 +203,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-ops", type=int, default=0,
                     help="run each op this many times (and a copy of known size), no timing")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="summarise the rocprofv3 runs under DIR into profiles/ (no GPU)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.profile_ops)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path would shard by batch or channel blocks with no exchange in the "
