@@ -36,6 +36,18 @@ __device__ __forceinline__ uint4 ld16(const void *p) {
 __device__ __forceinline__ void st16(void *p, uint4 v) {
   *reinterpret_cast<uint4 *>(p) = v;
 }
+// Non-temporal (streaming) forms.  Which streams of a kernel take them is a
+// measured choice: on MI355X a kernel runs fastest when part of its streams
+// are non-temporal, and slower when all or none are.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16nt(const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16nt(void *p, uint4 v) {
+  const u32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t *>(p));
+}
 
 template <typename E> __device__ __forceinline__ void unpack(uint4 r, float (&o)[Vw<E>::n]);
 template <> __device__ __forceinline__ void unpack<float>(uint4 r, float (&o)[4]) {
@@ -68,20 +80,29 @@ template <typename E, int N> struct RowBits {
   uint32_t d[dwords > 0 ? dwords : 1];
 };
 
-template <typename E, int N>
+// NTL: non-temporal loads (the 16- and 8-byte forms)
+template <typename E, int N, bool NTL = false>
 __device__ __forceinline__ RowBits<E, N> ld_row(const E *p) {
   RowBits<E, N> r;
   constexpr int bytes = N * (int)sizeof(E);
   if constexpr (bytes % 16 == 0) {
 #pragma unroll
     for (int i = 0; i < bytes / 16; ++i) {
-      uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+      const uint4 v = NTL ? ld16nt(reinterpret_cast<const uint4 *>(p) + i)
+                          : reinterpret_cast<const uint4 *>(p)[i];
       r.d[4 * i] = v.x; r.d[4 * i + 1] = v.y; r.d[4 * i + 2] = v.z; r.d[4 * i + 3] = v.w;
     }
   } else if constexpr (bytes % 8 == 0) {
 #pragma unroll
     for (int i = 0; i < bytes / 8; ++i) {
-      uint2 v = reinterpret_cast<const uint2 *>(p)[i];
+      uint2 v;
+      if constexpr (NTL) {
+        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p) + i);
+        v = make_uint2(t.x, t.y);
+      } else {
+        v = reinterpret_cast<const uint2 *>(p)[i];
+      }
       r.d[2 * i] = v.x; r.d[2 * i + 1] = v.y;
     }
   } else if constexpr (bytes % 4 == 0) {

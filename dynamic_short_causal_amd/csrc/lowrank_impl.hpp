@@ -198,7 +198,8 @@ __device__ __forceinline__ void gen_tap(
 // 32 token rows, the lanes compute in the token-per-lane layout reading the
 // ring, and the 16 x CB slab of y goes back through an LDS staging tile with
 // the same row-major thread mapping.  Loading and storing per lane (16 token
-// rows of 64 bytes per instruction) ran at two thirds of this speed.
+// rows of 64 bytes per instruction) ran at two thirds of this speed.  x is
+// loaded and y stored non-temporally (each is touched once per call).
 template <typename E, int W, int GPV> struct LrFwdGeo {
   using Gm = LrGeo<E, W, GPV>;
   static constexpr int XR = Gm::CB * 4 + 16;               // ring row pitch (fp32)
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
   for (int p = 0; p < NPASS; ++p) {
     const int tb = t0 - 16 + p * RPP + rr;
     const bool ok = tb >= 0 && cc_ok;
-    ring_put(tb, ld16(x + (ok ? (seq + tb) * D + cc : 0)), ok);
+    ring_put(tb, ld16nt(x + (ok ? (seq + tb) * D + cc : 0)), ok);
   }
   // Loads of one tile go to one of PF prefetch slots, PF tiles ahead; they are
   // branch-free (a thread without a token or channel reads row 0, zeroed later).
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
       const int tr = t + p * RPP + rr;
-      xn[sl][p] = ld16(x + (tr < t1 && cc_ok ? (seq + tr) * D + cc : 0));
+      xn[sl][p] = ld16nt(x + (tr < t1 && cc_ok ? (seq + tr) * D + cc : 0));
     }
   };
   // Per tile: fill the ring rows of the tile; barrier; taps, outputs to the
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
     for (int p = 0; p < NPASS; ++p) {
       const int r = p * RPP + rr;
       const uint4 val = *reinterpret_cast<const uint4 *>(stage + r * SP + vv * 16);
-      if (t + r < t1 && cc_ok) st16(y + (seq + t + r) * D + cc, val);
+      if (t + r < t1 && cc_ok) st16nt(y + (seq + t + r) * D + cc, val);
     }
   };
 #pragma unroll
@@ -358,6 +359,9 @@ __device__ __forceinline__ brsrc mk_rsrc(const void *p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
 }
 constexpr uint32_t kOOB = 0x80000000u;
+// cache-policy operand of the buffer accesses: non-temporal (x, dy, dx are
+// each touched once per call)
+constexpr int kNT = 2;
 
 template <typename E, int W, int GPV> struct LrBwdGeo {
   using Gm = LrGeo<E, W, GPV>;
@@ -538,12 +542,12 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
     const brsrc rdy = slab(dy, t, T);
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
-      dyn[sl][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rdy, voff[p], 0, 0));
+      dyn[sl][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rdy, voff[p], 0, kNT));
     if (ACT || !halo) {
       const brsrc rx = slab(x, t, T);
 #pragma unroll
       for (int p = 0; p < NPASS; ++p)
-        xn[sl][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff[p], 0, 0));
+        xn[sl][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff[p], 0, kNT));
     }
     const brsrc rz = zslab(t, T);
     if constexpr (BF) zn[sl] = (E)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
@@ -753,7 +757,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
 #pragma unroll
       for (int p = 0; p < NPASS; ++p) {
         const uint4 val = *reinterpret_cast<const uint4 *>(dxstage + (p * RPP + rr) * SP + vv * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, val), rdx, voff[p], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, val), rdx, voff[p], 0, kNT);
       }
     }
     if (!halo && wave == 0 && tau < t1) {
