@@ -1,0 +1,327 @@
+// lowrank_bwd_cl.hpp -- low-rank backward for per-channel filters (H = 1,
+// bf16), one channel per lane.
+//
+// Operation: the derivative of the low-rank dynamic short convolution (gist.science
+// summary "Dynamische Korte Convoluties Verbeteren Transformers", Methodologie >
+// Dynamische Korte Convoluties, Parametrisatie 1, and Efficiente
+// Trainingsimplementatie, bullet "Fused Low-Rank Kernel"):
+//   ds = dy (or dy * SiLU'(s)),  dx[t] = rho dy[t] + sum_k w[t+k,.,k] ds[t+k],
+//   dw[t,c,k] = ds[t,c] x[t-k,c],  dz = dw U^T,  dU = z^T dw.
+//
+// Layout.  A workgroup of 4 waves owns 128 channels and a chunk of tokens and
+// walks it in 16-token steps.  Each wave owns two groups of 16 channels.  In a
+// group, lane (q, n) (q = lane / 16, n = lane % 16) owns channel n and the four
+// consecutive tokens 4q..4q+3 of the step: exactly the output layout of a 16x16
+// MFMA whose rows are tokens and whose columns are channels.  So
+//   * filters come from MFMAs with A = z (rows = tokens, K = ranks) and
+//     B = U (K = ranks, columns = this group's channels), one per tap; for dx
+//     the A rows are z of tokens t+k ("shifted filters");
+//   * the causal taps of the lane's own tokens are in its registers; x and ds
+//     of the neighbouring tokens come from LDS;
+//   * dU[rank][channel] += z^T dw needs no transpose: the lane's four dw values
+//     (K = its four tokens) are the B operand as they stand;
+//   * dz^T = U dw^T contracts over channels, so dw goes through LDS once, read
+//     back with the transposing LDS read (ds_read_b64_tr_b16);
+//   * x and dy come from LDS slabs filled by row-major loads, read with the
+//     transposing read, which turns four token rows of one channel into one
+//     lane's four values.
+// Compared with one token per lane, each element costs about half the vector-
+// ALU instructions and LDS bytes; it runs 16 % faster at the QKV shape.  Tied
+// heads (H > 1) would turn every channel into a filter slot (H times the dz/dU
+// MFMA work), so they stay on the token-per-lane kernel.
+//
+// Rows past the sequence are handled by buffer resources (read as zero, not
+// written); the partials of dz (per channel block) and dU (per chunk) are the
+// same as those of the token-per-lane kernel and are reduced by the same
+// kernel.
+#pragma once
+#include "lowrank_impl.hpp"
+
+namespace dsc {
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+// Transposing LDS read (gfx950): in each 16-lane group, lane l receives element
+// l % 4 of the 8-byte chunks addressed by lanes 4e + l / 4, e = 0..3.  When lane
+// s addresses the chunk (row r0 + s/4, columns c0 + 4(s%4) .. +3) of a 16-bit
+// row-major array, lane l receives column c0 + l of rows r0 .. r0+3.
+__device__ __forceinline__ s16x4 tr16(const unsigned char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4_t *)(__attribute__((address_space(3))) char *)(uintptr_t)p);
+}
+// bf16 bits -> float
+__device__ __forceinline__ float bf2f(short v) { return __uint_as_float((uint32_t)(uint16_t)v << 16); }
+
+constexpr int kClWaves = 4;
+constexpr int kClNG = 2;                       // 16-channel groups per wave
+constexpr int kClThreads = 64 * kClWaves;
+constexpr int kClCB = 16 * kClNG * kClWaves;   // 128 channels per workgroup
+
+template <int W> struct LrBwdClGeo {
+  static constexpr int XP = kClCB * 2 + 32;    // bf16 rows (x ring, dy slab, dx staging)
+  static constexpr int ZP = 40;                // z ring row: 16 ranks + 8 bytes
+  static constexpr int DSP = 32 * 4 + 16;      // ds ring row of one channel: 32 tokens fp32
+  static constexpr int NHQ = (W + 2) / 4;      // x halo quads
+  static constexpr int NDQ = (W + 6) / 4;      // ds quads for dx
+  static constexpr int CHK = W * 64 * 8;       // dw chunks of one wave and group
+  static constexpr int o_x = 0;
+  static constexpr int o_dy = o_x + 32 * XP;
+  static constexpr int o_dx = o_dy + 16 * XP;
+  static constexpr int o_z = o_dx + 16 * XP;
+  static constexpr int o_ds = o_z + 32 * ZP;
+  static constexpr int o_chk = o_ds + kClCB * DSP;
+  static constexpr int o_dz = o_chk + kClWaves * CHK;
+  static constexpr int bytes = o_dz + kClWaves * 64 * 16;
+};
+
+// Waves per SIMD: as many as the compiler fits without spilling (read off the
+// kernel resource-usage report; the register count grows with W).
+template <int W, bool ACT>
+constexpr int lr_bwd_cl_min_waves() {
+  if constexpr (ACT) return W <= 7 ? 2 : 1;
+  else return W <= 4 ? 3 : 2;
+}
+
+template <int W, bool ACT>
+__global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void lr_bwd_cl_kernel(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ z, const bf16 *__restrict__ U,
+    const bf16 *__restrict__ dy, bf16 *__restrict__ dx, float *__restrict__ dzp,
+    float *__restrict__ dUp, int T, int D, int H, int R, int TC, int nchunk, int ncb,
+    int64_t N, float rho) {
+  using Gc = LrBwdClGeo<W>;
+  constexpr int XP = Gc::XP, ZP = Gc::ZP, DSP = Gc::DSP, NHQ = Gc::NHQ, NDQ = Gc::NDQ, NG = kClNG;
+  constexpr int RP = 16;
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char *xring = smem + Gc::o_x, *dyslab = smem + Gc::o_dy, *dxst = smem + Gc::o_dx,
+                *zring = smem + Gc::o_z, *dsring = smem + Gc::o_ds;
+  float *dzbuf = reinterpret_cast<float *>(smem + Gc::o_dz);
+
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, n = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  unsigned char *chk = smem + Gc::o_chk + wave * Gc::CHK;
+  int bid = blockIdx.x;
+  const int cb = bid % ncb;
+  bid /= ncb;
+  const int chunk = bid % nchunk;
+  const int b = bid / nchunk;
+  const int t0 = chunk * TC, t1 = min(T, t0 + TC);
+  const int64_t seq = (int64_t)b * T;
+  const int G = D / H, GW = G * W;
+  // group u of this wave: channels cl0[u] + n of the block
+  int cl0[NG], gg[NG];
+  bool cok[NG];
+#pragma unroll
+  for (int u = 0; u < NG; ++u) {
+    cl0[u] = (wave * NG + u) * 16;
+    const int c = cb * kClCB + cl0[u] + n;
+    cok[u] = c < D;
+    gg[u] = cok[u] ? c / H : 0;
+  }
+
+  // coop: each thread moves one 16-byte vector of x and one of dy per step
+  const int cr = tid >> 4, cv = tid & 15;
+  const int cc = cb * kClCB + cv * 8;
+  const uint32_t coff = (cc < D ? (uint32_t)cc * 2 : kOOB) + (uint32_t)(cr * D * 2);
+  const bool z_on = tid < 16 * R;
+  const uint32_t zoff = z_on ? (uint32_t)tid * 2 : kOOB;
+  const int zr_tok = tid / (R > 0 ? R : 1), zr_rank = tid - zr_tok * (R > 0 ? R : 1);
+  auto slab = [&](const bf16 *base, int t, int lim, int width, int pitch) {
+    return mk_rsrc(base + (seq + t) * (int64_t)pitch, (int64_t)(min(lim, t + 16) - t) * width * 2);
+  };
+
+  for (int i = tid; i < 32 * ZP / 4; i += kClThreads) reinterpret_cast<uint32_t *>(zring)[i] = 0u;
+
+  s16x4 bu[NG][W], uz[NG][W];
+#pragma unroll
+  for (int u = 0; u < NG; ++u)
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      s16x4 f, h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q + e;
+        f[e] = (cok[u] && r < R) ? (short)U[(int64_t)r * GW + gg[u] * W + k] : (short)0;
+        const int ce = cb * kClCB + cl0[u] + 4 * q + e;
+        h[e] = (ce < D && n < R) ? (short)U[(int64_t)n * GW + (ce / H) * W + k] : (short)0;
+      }
+      bu[u][k] = f;
+      uz[u][k] = h;
+    }
+  f32x4 accU[NG][W];
+#pragma unroll
+  for (int u = 0; u < NG; ++u)
+#pragma unroll
+    for (int k = 0; k < W; ++k) accU[u][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int tiles = (t1 - t0 + 15) / 16;
+  const int nsteps = tiles + 1;
+  __syncthreads();
+  {
+    const int tb = t0 - 16;
+    const brsrc rx = slab(x, tb, tb < 0 ? tb : T, D, D);
+    const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, coff, 0, kNT));
+    *reinterpret_cast<uint4 *>(xring + ((tb + cr) & 31) * XP + cv * 16) = v;
+  }
+  auto tra = [&](const unsigned char *base, int row, int col0) {
+    return base + row * XP + (col0 + 4 * (n & 3)) * 2;
+  };
+
+  uint4 xn, dyn;
+  bf16 zn;
+  auto issue = [&](int st) {
+    const int t = t0 + 16 * st;
+    const bool halo = st == tiles;
+    const brsrc rz = slab(z, t, T, R, R);
+    const brsrc rd = slab(dy, t, T, D, D);
+    const brsrc rx = slab(x, t, T, D, D);
+    zn = (bf16)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
+    dyn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, coff, 0, kNT));
+    if (ACT || !halo) xn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, coff, 0, kNT));
+  };
+  auto fill = [&](int st) {
+    const int t = t0 + 16 * st;
+    const bool halo = st == tiles;
+    if (ACT || !halo) *reinterpret_cast<uint4 *>(xring + ((t + cr) & 31) * XP + cv * 16) = xn;
+    *reinterpret_cast<uint4 *>(dyslab + cr * XP + cv * 16) = dyn;
+    if (z_on) reinterpret_cast<bf16 *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn;
+  };
+
+  float dyp[NG][4] = {};
+  const float rho_tap = ACT ? 0.f : rho;
+  issue(0);
+  for (int st = 0; st < nsteps; ++st) {
+    const int t = t0 + 16 * st;
+    const bool halo = st == tiles;
+    fill(st);
+    if (st + 1 < nsteps) issue(st + 1);
+    __syncthreads();  // (1)
+    constexpr int X0 = 4 * NHQ;
+    float ds[NG][4], dyc[NG][4], xw[NG][4 * NHQ + 4];
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const s16x4 v = tr16(tra(dyslab, 4 * q + (n >> 2), cl0[u]));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dyc[u][e] = bf2f(v[e]);
+#pragma unroll
+      for (int h = 0; h <= NHQ; ++h) {
+        const int row = (t + 4 * q - 4 * NHQ + 4 * h + (n >> 2)) & 31;
+        const s16x4 xv = tr16(tra(xring, row, cl0[u]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xw[u][4 * h + e] = bf2f(xv[e]);
+      }
+    }
+    if constexpr (ACT) {
+      const s16x4 az = *reinterpret_cast<const s16x4 *>(zring + ((t + n) & 31) * ZP + 8 * q);
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        float sa[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          const f32x4 wk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(az, bu[u][k], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sa[e] = fmaf(wk[e], xw[u][X0 + e - k], sa[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ds[u][e] = dyc[u][e] * silu_grad_f(sa[e]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NG; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ds[u][e] = dyc[u][e];
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u)
+      *reinterpret_cast<f32x4 *>(dsring + (cl0[u] + n) * DSP + ((t + 4 * q) & 31) * 4) =
+          f32x4{ds[u][0], ds[u][1], ds[u][2], ds[u][3]};
+    __builtin_amdgcn_wave_barrier();
+    if (st > 0) {
+      s16x4 az[W];
+#pragma unroll
+      for (int k = 0; k < W; ++k)
+        az[k] = *reinterpret_cast<const s16x4 *>(zring + ((t - 16 + n + k) & 31) * ZP + 8 * q);
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        float dw[4 * NDQ];
+#pragma unroll
+        for (int h = 0; h < NDQ; ++h) {
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(dsring + (cl0[u] + n) * DSP + ((t - 16 + 4 * q + 4 * h) & 31) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dw[4 * h + e] = v[e];
+        }
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = ACT ? rho * dyp[u][e] : 0.f;
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          const float ini = k == 0 ? rho_tap : 0.f;
+          const f32x4 wk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(az[k], bu[u][k], f32x4{ini, ini, ini, ini}, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = fmaf(wk[e], dw[e + k], o[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<uint16_t *>(dxst + (4 * q + e) * XP + (cl0[u] + n) * 2) =
+              __builtin_bit_cast(uint16_t, (__bf16)o[e]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dyp[u][e] = dyc[u][e];
+    if (!halo) {
+      const s16x4 azt = tr16(zring + ((t + 4 * q + (n >> 2)) & 31) * ZP + 8 * (n & 3));
+      const int src = 16 * (n & 3) + 4 * q + (n >> 2);
+      f32x4 dzacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        s16x4 bdw[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          const uint32_t p0 = pack_bf16x2(ds[u][0] * xw[u][X0 - k], ds[u][1] * xw[u][X0 + 1 - k]);
+          const uint32_t p1 = pack_bf16x2(ds[u][2] * xw[u][X0 + 2 - k], ds[u][3] * xw[u][X0 + 3 - k]);
+          bdw[k] = __builtin_bit_cast(s16x4, make_uint2(p0, p1));
+          accU[u][k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(azt, bdw[k], accU[u][k], 0, 0, 0);
+        }
+        if (u > 0) __builtin_amdgcn_wave_barrier();  // previous group's chunk reads before these writes
+#pragma unroll
+        for (int k = 0; k < W; ++k) *reinterpret_cast<s16x4 *>(chk + (k * 64 + lane) * 8) = bdw[k];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          const s16x4 bt = tr16(chk + (k * 64 + src) * 8);
+          dzacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(uz[u][k], bt, dzacc, 0, 0, 0);
+        }
+      }
+      *reinterpret_cast<f32x4 *>(dzbuf + (wave * 64 + lane) * 4) = dzacc;
+    }
+    __syncthreads();  // (2)
+    if (st > 0) {
+      const brsrc rdx = slab(dx, t - 16, t1, D, D);
+      const uint4 v = *reinterpret_cast<const uint4 *>(dxst + cr * XP + cv * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rdx, coff, 0, kNT);
+    }
+    // dz: wave w sums ranks 4w..4w+3 over the 4 waves' tiles (lane j: token t + j)
+    if (!halo && lane < 16 && t + lane < t1) {
+      f32x4 s4 = *reinterpret_cast<const f32x4 *>(dzbuf + (16 * wave + lane) * 4);
+#pragma unroll
+      for (int w2 = 1; w2 < kClWaves; ++w2) s4 += *reinterpret_cast<const f32x4 *>(dzbuf + (w2 * 64 + 16 * wave + lane) * 4);
+      *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + t + lane) * RP + 4 * wave) = s4;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NG; ++u)
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      f32x4 v = accU[u][k];
+      for (int m = 1; m < H; m <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], m);
+      }
+      if (cok[u] && (n % H) == 0) {
+        float *dst = dUp + (int64_t)(b * nchunk + chunk) * RP * GW + gg[u] * W + k;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(int64_t)(4 * q + e) * GW] = v[e];
+      }
+    }
+}
+}  // namespace dsc

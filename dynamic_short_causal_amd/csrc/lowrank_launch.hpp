@@ -4,6 +4,7 @@
 // ---------------------------------------------------------------------------
 #pragma once
 #include "lowrank_impl.hpp"
+#include "lowrank_bwd_cl.hpp"
 
 namespace dsc {
 
@@ -24,25 +25,71 @@ static hipError_t launch_lr_fwd(const LrArgs &a) {
   return hipGetLastError();
 }
 
-template <typename E, int W, int GPV>
-static hipError_t launch_lr_bwd(const LrArgs &a) {
+template <typename E>
+static hipError_t launch_lr_reduce(const LrArgs &a, const LrBwdPlan &p, const float *dzp,
+                                   const float *dUp);
+
+// per-channel filters in bf16: one channel per lane (lowrank_bwd_cl.hpp)
+template <int W>
+static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
   hipStream_t s = (hipStream_t)a.stream;
   const float rho = a.residual ? 1.f : 0.f;
-  const int64_t GW = (a.D / a.H) * a.W;
   const LrBwdPlan p = lr_bwd_plan(a.B, a.T, a.D, a.W, a.H, a.R, a.bf16);
-  const int64_t N = a.B * a.T;
+  if (p.cb != kClCB) return hipErrorInvalidValue;  // same channel blocks as the plan
   float *dzp = (float *)a.ws;
   float *dUp = (float *)((char *)a.ws + p.dz_part);
   const int64_t nblocks = a.B * p.nchunk * p.ncb;
   if (nblocks > 0) {
-    constexpr int smem = LrBwdGeo<E, W, GPV>::bytes;
-    hipLaunchKernelGGL((lr_bwd_kernel<E, W, GPV>), dim3((unsigned)nblocks),
-                       dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
-                       (const E *)a.U, (const E *)a.dy, (E *)a.dx, dzp, dUp, (int)a.T, (int)a.D,
-                       a.R, p.tc, (int)p.nchunk, (int)p.ncb, N, rho, a.act ? 1 : 0);
+    constexpr int smem = LrBwdClGeo<W>::bytes;
+    const int64_t N = a.B * a.T;
+    if (a.act)
+      hipLaunchKernelGGL((lr_bwd_cl_kernel<W, true>), dim3((unsigned)nblocks), dim3(kClThreads),
+                         smem, s, (const bf16 *)a.x, (const bf16 *)a.z, (const bf16 *)a.U,
+                         (const bf16 *)a.dy, (bf16 *)a.dx, dzp, dUp, (int)a.T, (int)a.D, a.H,
+                         a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
+    else
+      hipLaunchKernelGGL((lr_bwd_cl_kernel<W, false>), dim3((unsigned)nblocks), dim3(kClThreads),
+                         smem, s, (const bf16 *)a.x, (const bf16 *)a.z, (const bf16 *)a.U,
+                         (const bf16 *)a.dy, (bf16 *)a.dx, dzp, dUp, (int)a.T, (int)a.D, a.H,
+                         a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  return launch_lr_reduce<bf16>(a, p, dzp, dUp);
+}
+
+template <typename E, int W, int GPV>
+static hipError_t launch_lr_bwd(const LrArgs &a) {
+  if constexpr (sizeof(E) == 2 && GPV == 8) {  // H == 1
+    return launch_lr_bwd_cl<W>(a);
+  } else {
+    hipStream_t s = (hipStream_t)a.stream;
+    const float rho = a.residual ? 1.f : 0.f;
+    const LrBwdPlan p = lr_bwd_plan(a.B, a.T, a.D, a.W, a.H, a.R, a.bf16);
+    const int64_t N = a.B * a.T;
+    float *dzp = (float *)a.ws;
+    float *dUp = (float *)((char *)a.ws + p.dz_part);
+    const int64_t nblocks = a.B * p.nchunk * p.ncb;
+    if (nblocks > 0) {
+      constexpr int smem = LrBwdGeo<E, W, GPV>::bytes;
+      hipLaunchKernelGGL((lr_bwd_kernel<E, W, GPV>), dim3((unsigned)nblocks),
+                         dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
+                         (const E *)a.U, (const E *)a.dy, (E *)a.dx, dzp, dUp, (int)a.T,
+                         (int)a.D, a.R, p.tc, (int)p.nchunk, (int)p.ncb, N, rho, a.act ? 1 : 0);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return launch_lr_reduce<E>(a, p, dzp, dUp);
+  }
+}
+
+// fixed-order sums of the dz and dU partials, cast to the output type
+template <typename E>
+static hipError_t launch_lr_reduce(const LrArgs &a, const LrBwdPlan &p, const float *dzp,
+                                   const float *dUp) {
+  hipStream_t s = (hipStream_t)a.stream;
+  const int64_t N = a.B * a.T;
+  const int64_t GW = (a.D / a.H) * a.W;
   const int64_t total = N * a.R + (int64_t)a.R * GW;
   int64_t grid = (total + 255) / 256;
   if (grid > 4096) grid = 4096;

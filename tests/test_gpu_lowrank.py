@@ -65,6 +65,8 @@ def test_ranks(dsc, orc, R):
                                           (True, True)])
 def test_epilogues(dsc, orc, residual, act):
     run_case(dsc, orc, 2, 97, 1024, 4, 8, 16, torch.bfloat16, residual, act, 7600)
+    # per-channel filters in bf16 take the one-channel-per-lane backward
+    run_case(dsc, orc, 2, 97, 392, 4, 1, 16, torch.bfloat16, residual, act, 7650)
     run_case(dsc, orc, 2, 97, 256, 4, 1, 16, torch.float32, residual, act, 7700)
 
 
