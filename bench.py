@@ -64,6 +64,7 @@ KERNEL_SOURCES = {
                     "dynamic_short_causal_amd/csrc/lowrank_launch.hpp",
                     "dynamic_short_causal_amd/csrc/dsc_device.hpp"],
     "lowrank_bwd": ["dynamic_short_causal_amd/csrc/lowrank_impl.hpp",
+                    "dynamic_short_causal_amd/csrc/lowrank_bwd_cl.hpp",
                     "dynamic_short_causal_amd/csrc/lowrank_launch.hpp",
                     "dynamic_short_causal_amd/csrc/dsc_launch.hpp",
                     "dynamic_short_causal_amd/csrc/dsc_device.hpp"],
@@ -122,7 +123,7 @@ OP_KERNELS = {  # op -> kernel names (rocprofv3) that one call launches
     "headwise_fwd": ["hw_fwd_kernel"],
     "headwise_bwd": ["hw_bwd_kernel"],
     "lowrank_fwd": ["lr_fwd_kernel"],
-    "lowrank_bwd": ["lr_bwd_kernel", "lr_reduce_kernel"],
+    "lowrank_bwd": ["lr_bwd_cl_kernel", "lr_bwd_kernel", "lr_reduce_kernel"],
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"  # the 512 MiB device copy of --profile-ops
 COPY_KIB = 524288
@@ -182,6 +183,7 @@ def summarize_profiles(d, calls):
               "| op | kernel | calls | avg us | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB |",
               "|---|---|---|---|---|---|---|"]
     for op, ks in OP_KERNELS.items():
+        ks = [k for k in ks if k in stats]  # the kernels this workload launched
         tot = 0.0
         for k in ks:
             n, us = stats.get(k, (0, float("nan")))
