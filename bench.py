@@ -329,6 +329,14 @@ def main():
                    "frac_of_peak": round(nbytes[n] / (per_kernel_ms[n] * 1e-3) / 1e9
                                          / HBM_PEAK_GBPS, 4),
                    "algorithmic_bytes": nbytes[n]} for n in names}
+    # per variant, as the metric is defined for each (tokens / (t_fwd + t_bwd))
+    variants = {}
+    for v, (f, bwd) in {"headwise": ("headwise_fwd", "headwise_bwd"),
+                        "lowrank": ("lowrank_fwd", "lowrank_bwd")}.items():
+        t = (per_kernel_ms[f] + per_kernel_ms[bwd]) * 1e-3
+        gbps = (nbytes[f] + nbytes[bwd]) / t / 1e9
+        variants[v] = {"tokens_per_s": round(tokens / t, 1), "gbps": round(gbps, 1),
+                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
     out = {
         "metric": "fwd+bwd tokens/s + achieved HBM GB/s (% of peak), D=6144 T=2048 W=4",
         "value": round(tokens / (ms_per_step * 1e-3), 1),
@@ -350,6 +358,7 @@ def main():
         "pct_of_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "copy_gbps": round(copy_gbps, 1),
         "kernels": kernels,
+        "variants": variants,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
