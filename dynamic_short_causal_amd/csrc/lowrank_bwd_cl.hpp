@@ -51,6 +51,45 @@ __device__ __forceinline__ s16x4 tr16(const unsigned char *p) {
 // bf16 bits -> float
 __device__ __forceinline__ float bf2f(short v) { return __uint_as_float((uint32_t)(uint16_t)v << 16); }
 
+// N consecutive 16-bit values from p (zeros when !ok), with the widest loads
+// the alignment of p allows (p is aligned to 2N bytes rounded down to a power
+// of two, up to 16, at every call site)
+template <int N>
+__device__ __forceinline__ void load_shorts(const bf16 *p, bool ok, short (&o)[N]) {
+  constexpr int B = (N % 8 == 0) ? 8 : (N % 4 == 0) ? 4 : (N % 2 == 0) ? 2 : 1;
+#pragma unroll
+  for (int i = 0; i < N; i += B) {
+    if constexpr (B == 8) {
+      const uint4 v = ok ? *reinterpret_cast<const uint4 *>(p + i) : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[i + j] = (short)(w[j >> 1] >> (16 * (j & 1)));
+    } else if constexpr (B == 4) {
+      const uint2 v = ok ? *reinterpret_cast<const uint2 *>(p + i) : make_uint2(0u, 0u);
+      const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[i + j] = (short)(w[j >> 1] >> (16 * (j & 1)));
+    } else if constexpr (B == 2) {
+      const uint32_t v = ok ? *reinterpret_cast<const uint32_t *>(p + i) : 0u;
+      o[i] = (short)v;
+      o[i + 1] = (short)(v >> 16);
+    } else {
+      o[i] = ok ? (short)p[i] : (short)0;
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ void store_floats(float *p, const float (&v)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<f32x4 *>(p + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) p[i] = v[i];
+  }
+}
+
 constexpr int kClWaves = 4;
 constexpr int kClNG = 2;                       // 16-channel groups per wave
 constexpr int kClThreads = 64 * kClWaves;
@@ -85,7 +124,7 @@ template <int W, bool ACT>
 __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void lr_bwd_cl_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ z, const bf16 *__restrict__ U,
     const bf16 *__restrict__ dy, bf16 *__restrict__ dx, float *__restrict__ dzp,
-    float *__restrict__ dUp, int T, int D, int H, int R, int TC, int nchunk, int ncb,
+    float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk, int ncb,
     int64_t N, float rho) {
   using Gc = LrBwdClGeo<W>;
   constexpr int XP = Gc::XP, ZP = Gc::ZP, DSP = Gc::DSP, NHQ = Gc::NHQ, NDQ = Gc::NDQ, NG = kClNG;
@@ -105,16 +144,14 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
   const int b = bid / nchunk;
   const int t0 = chunk * TC, t1 = min(T, t0 + TC);
   const int64_t seq = (int64_t)b * T;
-  const int G = D / H, GW = G * W;
+  const int GW = D * W;  // U columns (one filter per channel)
   // group u of this wave: channels cl0[u] + n of the block
-  int cl0[NG], gg[NG];
+  int cl0[NG];
   bool cok[NG];
 #pragma unroll
   for (int u = 0; u < NG; ++u) {
     cl0[u] = (wave * NG + u) * 16;
-    const int c = cb * kClCB + cl0[u] + n;
-    cok[u] = c < D;
-    gg[u] = cok[u] ? c / H : 0;
+    cok[u] = cb * kClCB + cl0[u] + n < D;
   }
 
   // coop: each thread moves one 16-byte vector of x and one of dy per step
@@ -130,22 +167,30 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
 
   for (int i = tid; i < 32 * ZP / 4; i += kClThreads) reinterpret_cast<uint32_t *>(zring)[i] = 0u;
 
+  // Resident U fragments per group u and tap k:
+  //  bu: filter B operand, lane (q, n): U[ranks 4q..4q+3][c*W + k] (c = its channel);
+  //      row r of U holds the W taps of channel c contiguously;
+  //  uz: dz A operand, lane (q, n): U[rank n][(c4+e)*W + k], e = 0..3, where
+  //      c4 = the group's channel 4q: 4W contiguous values of row n.
   s16x4 bu[NG][W], uz[NG][W];
 #pragma unroll
-  for (int u = 0; u < NG; ++u)
+  for (int u = 0; u < NG; ++u) {
+    const int c = cb * kClCB + cl0[u] + n;
+    short tb[4][W];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * q + e;
+      load_shorts<W>(U + (int64_t)r * GW + (int64_t)c * W, cok[u] && r < R, tb[e]);
+    }
+    const int c4 = cb * kClCB + cl0[u] + 4 * q;
+    short tz[4 * W];
+    load_shorts<4 * W>(U + (int64_t)n * GW + (int64_t)c4 * W, c4 < D && n < R, tz);
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-      s16x4 f, h;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * q + e;
-        f[e] = (cok[u] && r < R) ? (short)U[(int64_t)r * GW + gg[u] * W + k] : (short)0;
-        const int ce = cb * kClCB + cl0[u] + 4 * q + e;
-        h[e] = (ce < D && n < R) ? (short)U[(int64_t)n * GW + (ce / H) * W + k] : (short)0;
-      }
-      bu[u][k] = f;
-      uz[u][k] = h;
+      bu[u][k] = s16x4{tb[0][k], tb[1][k], tb[2][k], tb[3][k]};
+      uz[u][k] = s16x4{tz[k], tz[W + k], tz[2 * W + k], tz[3 * W + k]};
     }
+  }
   f32x4 accU[NG][W];
 #pragma unroll
   for (int u = 0; u < NG; ++u)
@@ -308,20 +353,20 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
       *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + t + lane) * RP + 4 * wave) = s4;
     }
   }
+  // dU partial of this chunk: lane (q, n) holds ranks 4q..4q+3 of channel c,
+  // every tap; a rank row of U has channel c's W taps contiguously
+  float *dst = dUp + (int64_t)(b * nchunk + chunk) * RP * GW;
 #pragma unroll
-  for (int u = 0; u < NG; ++u)
+  for (int u = 0; u < NG; ++u) {
+    if (!cok[u]) continue;
+    const int c = cb * kClCB + cl0[u] + n;
 #pragma unroll
-    for (int k = 0; k < W; ++k) {
-      f32x4 v = accU[u][k];
-      for (int m = 1; m < H; m <<= 1) {
+    for (int e = 0; e < 4; ++e) {
+      float v[W];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], m);
-      }
-      if (cok[u] && (n % H) == 0) {
-        float *dst = dUp + (int64_t)(b * nchunk + chunk) * RP * GW + gg[u] * W + k;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(int64_t)(4 * q + e) * GW] = v[e];
-      }
+      for (int k = 0; k < W; ++k) v[k] = accU[u][k][e];
+      store_floats<W>(dst + (int64_t)(4 * q + e) * GW + (int64_t)c * W, v);
     }
+  }
 }
 }  // namespace dsc

@@ -35,7 +35,7 @@ static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
   hipStream_t s = (hipStream_t)a.stream;
   const float rho = a.residual ? 1.f : 0.f;
   const LrBwdPlan p = lr_bwd_plan(a.B, a.T, a.D, a.W, a.H, a.R, a.bf16);
-  if (p.cb != kClCB) return hipErrorInvalidValue;  // same channel blocks as the plan
+  if (p.cb != kClCB || a.H != 1) return hipErrorInvalidValue;  // the plan's channel blocks
   float *dzp = (float *)a.ws;
   float *dUp = (float *)((char *)a.ws + p.dz_part);
   const int64_t nblocks = a.B * p.nchunk * p.ncb;
@@ -45,12 +45,12 @@ static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
     if (a.act)
       hipLaunchKernelGGL((lr_bwd_cl_kernel<W, true>), dim3((unsigned)nblocks), dim3(kClThreads),
                          smem, s, (const bf16 *)a.x, (const bf16 *)a.z, (const bf16 *)a.U,
-                         (const bf16 *)a.dy, (bf16 *)a.dx, dzp, dUp, (int)a.T, (int)a.D, a.H,
+                         (const bf16 *)a.dy, (bf16 *)a.dx, dzp, dUp, (int)a.T, (int)a.D,
                          a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
     else
       hipLaunchKernelGGL((lr_bwd_cl_kernel<W, false>), dim3((unsigned)nblocks), dim3(kClThreads),
                          smem, s, (const bf16 *)a.x, (const bf16 *)a.z, (const bf16 *)a.U,
-                         (const bf16 *)a.dy, (bf16 *)a.dx, dzp, dUp, (int)a.T, (int)a.D, a.H,
+                         (const bf16 *)a.dy, (bf16 *)a.dx, dzp, dUp, (int)a.T, (int)a.D,
                          a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
