@@ -45,6 +45,11 @@ def _declare(lib):
                                     _int, _int, _int, _i64, _lp, _dp, _dp],
         "oracle_lowrank_dU_cols": [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _int, _int, _int,
                                    _int, _i64, _lp, _dp],
+        "oracle_headwise_decode": [_dp, _dp, _dp, _dp, _dp, _i64, _i64, _int, _int, _int,
+                                   _int],
+        "oracle_lowrank_decode": [_dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _int, _int,
+                                  _int, _int, _int],
+        "oracle_decode_state": [_dp, _dp, _i64, _i64, _i64, _int],
         "oracle_num_threads": [],
         "oracle_set_num_threads": [_int],
     }
@@ -199,6 +204,39 @@ class Oracle:
                                         int(act), len(c), cp, _p(out))
         return out
 
+    # ---- one-token steps (inference) -------------------------------------
+    def headwise_decode(self, x, w, state, H, residual=False, act=False):
+        """x (B,D), w (B,G,W), state (B,W-1,D) -> (y (B,D), new state)."""
+        x, w, state = _c(x), _c(w), _c(state)
+        B, D = x.shape
+        W = w.shape[-1]
+        assert w.shape == (B, D // H, W) and state.shape == (B, W - 1, D)
+        y = np.empty_like(x)
+        out = np.empty_like(state)
+        self.lib.oracle_headwise_decode(_p(x), _p(w), _p(state), _p(out), _p(y), B, D, W,
+                                        H, int(residual), int(act))
+        return y, out
+
+    def lowrank_decode(self, x, z, U, state, W, H, residual=False, act=False):
+        """x (B,D), z (B,R), U (R,G*W), state (B,W-1,D) -> (y, new state)."""
+        x, z, U, state = _c(x), _c(z), _c(U), _c(state)
+        B, D = x.shape
+        R = z.shape[-1]
+        assert U.shape == (R, (D // H) * W) and state.shape == (B, W - 1, D)
+        y = np.empty_like(x)
+        out = np.empty_like(state)
+        self.lib.oracle_lowrank_decode(_p(x), _p(z), _p(U), _p(state), _p(out), _p(y), B,
+                                       D, W, H, R, int(residual), int(act))
+        return y, out
+
+    def decode_state(self, x, W):
+        """State (B, W-1, D) after the prompt x (B, T, D)."""
+        x = _c(x)
+        B, T, D = x.shape
+        st = np.empty((B, W - 1, D))
+        self.lib.oracle_decode_state(_p(x), _p(st), B, T, D, W)
+        return st
+
 
 _DEFAULT = None
 
@@ -209,3 +247,4 @@ def default():
     if _DEFAULT is None:
         _DEFAULT = Oracle()
     return _DEFAULT
+

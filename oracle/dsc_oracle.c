@@ -414,3 +414,63 @@ void oracle_lowrank_dU_cols(const double *x, const double *z, const double *U,
     free(wg);
   }
 }
+
+/*
+ * Streaming evaluation (one token at a time, for inference).  The pages define
+ * the convolution over a whole sequence ([gist] Mechanisme) and leave inference
+ * as open work ([wisp] Limitations).  The reading taken here: a step evaluates
+ * the same causal sum at the newest position t, with the W-1 previous inputs
+ * kept as a state
+ *   state[b, j, c] = x[b, t-(W-1)+j, c],  j = 0 .. W-2 (oldest first),
+ *                    zero for positions before the start of the sequence;
+ *   y[b, c] = act(sum_{k<W} w[b, g(c), k] * x_{t-k}[b, c]) + rho * x_t[b, c],
+ *   x_{t-0} = x_t,  x_{t-k} = state[b, W-1-k, c] for k >= 1;
+ * afterwards the state drops its oldest row and appends x_t.
+ * Layouts: x, y (B, D); w (B, G, W); state_in, state_out (B, W-1, D).
+ */
+void oracle_headwise_decode(const double *x, const double *w,
+                            const double *state_in, double *state_out,
+                            double *y, int64_t B, int64_t D, int W, int H,
+                            int residual, int act) {
+  int64_t G = D / H;
+  int S = W - 1;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t c = 0; c < D; ++c) {
+      int64_t g = c / H;
+      double s = w[(b * G + g) * W + 0] * x[b * D + c];
+      for (int k = 1; k < W; ++k)
+        s += w[(b * G + g) * W + k] * state_in[(b * S + (S - k)) * D + c];
+      y[b * D + c] = act_fn(s, act) + (residual ? x[b * D + c] : 0.0);
+      for (int j = 0; j + 1 < S; ++j)
+        state_out[(b * S + j) * D + c] = state_in[(b * S + j + 1) * D + c];
+      if (S > 0) state_out[(b * S + S - 1) * D + c] = x[b * D + c];
+    }
+  }
+}
+
+/* Low-rank step: w[b,g,k] = sum_r z[b,r] * U[r, g*W+k] ([gist] Parametrisatie
+ * 1), then the head-wise step.  z (B, R), U (R, G*W). */
+void oracle_lowrank_decode(const double *x, const double *z, const double *U,
+                           const double *state_in, double *state_out,
+                           double *y, int64_t B, int64_t D, int W, int H, int R,
+                           int residual, int act) {
+  int64_t G = D / H;
+  double *w = (double *)malloc(sizeof(double) * (size_t)(B * G * W));
+  if (!w) return;
+  oracle_lowrank_w(z, U, w, B, 1, G, W, R);
+  oracle_headwise_decode(x, w, state_in, state_out, y, B, D, W, H, residual, act);
+  free(w);
+}
+
+/* State after a prompt x (B, T, D): its last W-1 rows, zero where the prompt
+ * is shorter than W-1. */
+void oracle_decode_state(const double *x, double *state, int64_t B, int64_t T,
+                         int64_t D, int W) {
+  int S = W - 1;
+  for (int64_t b = 0; b < B; ++b)
+    for (int j = 0; j < S; ++j) {
+      int64_t t = T - S + j;
+      for (int64_t c = 0; c < D; ++c)
+        state[(b * S + j) * D + c] = t >= 0 ? x[IDX3(b, t, c, T, D)] : 0.0;
+    }
+}

@@ -333,8 +333,53 @@ def pin_sampled_match_full(orc):
                rtol=1e-12, atol=1e-12, what="dU cols")
 
 
+
+# ---------------------------------------------------------------- streaming steps
+def pin_decode_handworked(orc):
+    """One step worked by hand (tests/golden/handworked.json, "decode")."""
+    d = json.load(open(GOLDEN))["decode"]
+    st, x = np.array(d["state"], float), np.array(d["x"], float)
+    y, st2 = orc.headwise_decode(x, np.array(d["per_channel_w"], float), st, 1)
+    _close(y, d["y"], what="decode y")
+    _close(st2, d["state_after"], what="decode state")
+    y, _ = orc.headwise_decode(x, np.array(d["per_channel_w"], float), st, 1, residual=True)
+    _close(y, d["y_residual"], what="decode y+x")
+    y, _ = orc.headwise_decode(x, np.array(d["tied_H2_w"], float), st, 2)
+    _close(y, d["tied_H2_y"], what="decode tied y")
+    y, _ = orc.lowrank_decode(x, np.array(d["lowrank_H2_R1_z"], float),
+                              np.array(d["lowrank_H2_R1_U"], float), st, d["W"], 2)
+    _close(y, d["tied_H2_y"], what="decode low-rank y")
+    _close(orc.decode_state(np.array(d["prompt_short"], float), d["W"]), d["state_short"],
+           what="state after a short prompt")
+    _close(orc.decode_state(np.array(d["prompt_long"], float), d["W"]), d["state_long"],
+           what="state after a long prompt")
+
+
+def pin_decode_rolls_forward(orc):
+    """Stepping token by token from an empty state reproduces the whole-sequence
+    forward at every position, and the state is always the last W-1 inputs."""
+    rng = _rng(31)
+    for (B, T, D, W, H, res, act) in [(2, 9, 6, 3, 2, True, True), (1, 7, 4, 4, 1, False, False),
+                                      (2, 5, 8, 1, 4, True, False)]:
+        x = _rand(rng, B, T, D)
+        w = _rand(rng, B, T, D // H, W, std=0.5)
+        y = orc.headwise_fwd(x, w, H, residual=res, act=act)
+        st = np.zeros((B, W - 1, D))
+        for t in range(T):
+            yt, st = orc.headwise_decode(x[:, t], w[:, t], st, H, residual=res, act=act)
+            _close(yt, y[:, t], what=f"decode t={t}")
+            _close(st, orc.decode_state(x[:, :t + 1], W), what=f"state t={t}")
+        R = 3
+        z = _rand(rng, B, T, R)
+        U = _rand(rng, R, (D // H) * W, std=0.5)
+        yl = orc.lowrank_fwd(x, z, U, W, H, residual=res, act=act)
+        for T0 in sorted({0, 1, max(0, W - 2), T - 1}):
+            st = orc.decode_state(x[:, :T0], W)
+            yt, _ = orc.lowrank_decode(x[:, T0], z[:, T0], U, st, W, H, residual=res, act=act)
+            _close(yt, yl[:, T0], what=f"low-rank decode after a {T0}-token prompt")
+
 ALL_PINS = [pin_handworked, pin_width_one_is_scale, pin_silu_values,
             pin_static_filter_is_conv1d, pin_causality, pin_linearity,
             pin_residual_is_tap0_shift, pin_tying_is_repeat, pin_lowrank_is_headwise,
             pin_adjoint, pin_euler, pin_finite_differences, pin_torch_autograd,
-            pin_sampled_match_full]
+            pin_sampled_match_full, pin_decode_handworked, pin_decode_rolls_forward]

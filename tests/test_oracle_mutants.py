@@ -40,6 +40,11 @@ MUTANTS = {
                    "acc += dw[n * GW + col];"),
     "dU_drops_z": ("for (int64_t n = 0; n < N; ++n) acc += z[n * R + r] * dw[n * GW + col];",
                    "for (int64_t n = 0; n < N; ++n) acc += dw[n * GW + col];"),
+    "decode_tap_order": ("s += w[(b * G + g) * W + k] * state_in[(b * S + (S - k)) * D + c];",
+                         "s += w[(b * G + g) * W + k] * state_in[(b * S + (k - 1)) * D + c];"),
+    "decode_no_shift": ("state_out[(b * S + j) * D + c] = state_in[(b * S + j + 1) * D + c];",
+                        "state_out[(b * S + j) * D + c] = state_in[(b * S + j) * D + c];"),
+    "decode_state_offset": ("int64_t t = T - S + j;", "int64_t t = T - S + j - 1;"),
     "residual_twice": ("y[n * D + c] = act_fn(s, act) + (residual ? x[n * D + c] : 0.0);\n    }\n  }\n}",
                        "y[n * D + c] = act_fn(s, act) + (residual ? 2.0 * x[n * D + c] : 0.0);\n    }\n  }\n}"),
 }
