@@ -205,6 +205,42 @@ def summarize_profiles(d, calls):
     print("\n".join(lines))
 
 
+def decode_bench(dsc, di, torch, dev, stream, iters=200):
+    """One-token steps at serving batches: mean time per step over `iters`
+    back-to-back launches on one stream (HIP events), for head-wise H=16 and
+    low-rank R=16 H=1 at D=6144, W=4, bf16, residual.  Not part of the step."""
+    D, W, R = WORKLOAD["D"], WORKLOAD["W"], WORKLOAD["R"]
+    Hh, Hl = WORKLOAD["H_headwise"], WORKLOAD["H_lowrank"]
+    out = {}
+    for B in (64, 512):
+        x = di.randn((B, D), 1.0, 90, "bf16").to(dev)
+        st = di.randn((B, W - 1, D), 1.0, 91, "bf16").to(dev)
+        w = di.randn((B, D // Hh, W), 0.5, 92, "bf16").to(dev)
+        z = di.randn((B, R), 1.0, 93, "bf16").to(dev)
+        U = di.randn((R, (D // Hl) * W), 0.125, 94, "bf16").to(dev)
+        y = torch.empty_like(x)
+        act_bytes = 2 * B * D * (2 + 2 * (W - 1))
+        hw = lambda: dsc.dsc_headwise_decode(x, w, st, y, Hh, True, False, stream)
+        lr = lambda: dsc.dsc_lowrank_decode(x, z, U, st, y, W, Hl, True, False, stream)
+        cases = {"headwise": (hw, act_bytes + 2 * B * (D // Hh) * W),
+                 "lowrank": (lr, act_bytes + 2 * (B * R + R * (D // Hl) * W))}
+        for name, (fn, nbytes) in cases.items():
+            for _ in range(10):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(iters):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / iters
+            out[f"{name}_B{B}"] = {"us_per_step": round(us, 2),
+                                   "tokens_per_s": round(B / (us * 1e-6), 1),
+                                   "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                   "algorithmic_bytes": nbytes}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +354,9 @@ def main():
     copy_gbps = 2 * src.numel() * 2 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
+    print("bench: timing decode steps", file=sys.stderr, flush=True)
+    decode = decode_bench(dsc, di, torch, dev, stream)
+
     nbytes = algorithmic_bytes(B, T, D, W, Hh, R, Hl)
     ms_per_step = elapsed / args.steps * 1e3
     tokens = B * T
@@ -359,6 +398,7 @@ def main():
         "copy_gbps": round(copy_gbps, 1),
         "kernels": kernels,
         "variants": variants,
+        "decode": decode,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

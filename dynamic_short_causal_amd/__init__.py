@@ -24,7 +24,8 @@ DSC_RESIDUAL, DSC_ACT_SILU = 1, 2
 # every symbol declared in include/dsc.h
 EXPORTS = ("dsc_version", "dsc_status_string", "dsc_last_error", "dsc_headwise_fwd",
            "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd_workspace_bytes",
-           "dsc_lowrank_bwd")
+           "dsc_lowrank_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
+           "dsc_decode_state")
 
 
 class DscError(RuntimeError):
@@ -51,8 +52,12 @@ def _load():
     lib.dsc_lowrank_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.dsc_lowrank_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
                                     i64, ci, ci, ci, ci, cu, vp]
+    lib.dsc_headwise_decode.argtypes = [vp, vp, vp, vp, i64, i64, ci, ci, ci, cu, vp]
+    lib.dsc_lowrank_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, ci, cu, vp]
+    lib.dsc_decode_state.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
     for name in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd",
-                 "dsc_lowrank_bwd"):
+                 "dsc_lowrank_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
+                 "dsc_decode_state"):
         getattr(lib, name).restype = ci
     return lib
 
@@ -159,6 +164,40 @@ def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace, W, H, residual=False, ac
     return dx, dz, dU
 
 
+def dsc_headwise_decode(x, w, state, y, H, residual=False, act=False, stream=None):
+    """One token: x (B, D), w (B, G, W); state (B, W-1, D) is advanced in place."""
+    B, D = x.shape
+    W = w.shape[-1]
+    for n, t, s in (("x", x, (B, D)), ("w", w, (B, D // H, W)), ("state", state, (B, W - 1, D)),
+                    ("y", y, (B, D))):
+        _need(t, n, s, x.dtype)
+    _check(LIB.dsc_headwise_decode(_ptr(x), _ptr(w), _ptr(state), _ptr(y), B, D, W, H,
+                                   _dtype(x), _flags(residual, act), _stream(stream)))
+    return y
+
+
+def dsc_lowrank_decode(x, z, U, state, y, W, H, residual=False, act=False, stream=None):
+    """One token: x (B, D), z (B, R), U (R, G*W); state (B, W-1, D) advanced in place."""
+    B, D = x.shape
+    R = z.shape[-1]
+    for n, t, s in (("x", x, (B, D)), ("z", z, (B, R)), ("U", U, (R, (D // H) * W)),
+                    ("state", state, (B, W - 1, D)), ("y", y, (B, D))):
+        _need(t, n, s, x.dtype)
+    _check(LIB.dsc_lowrank_decode(_ptr(x), _ptr(z), _ptr(U), _ptr(state), _ptr(y), B, D, W, H,
+                                  R, _dtype(x), _flags(residual, act), _stream(stream)))
+    return y
+
+
+def dsc_decode_state(x, state, stream=None):
+    """The (B, W-1, D) state left by a prompt x (B, T, D)."""
+    B, T, D = x.shape
+    W = state.shape[1] + 1
+    for n, t, s in (("x", x, (B, T, D)), ("state", state, (B, W - 1, D))):
+        _need(t, n, s, x.dtype)
+    _check(LIB.dsc_decode_state(_ptr(x), _ptr(state), B, T, D, W, _dtype(x), _stream(stream)))
+    return state
+
+
 # --------------------------------------------------------------- allocating forms
 def headwise_fwd(x, w, H, residual=False, act=False, stream=None):
     return dsc_headwise_fwd(x, w, torch.empty_like(x), H, residual, act, stream)
@@ -184,3 +223,16 @@ def lowrank_bwd(x, z, U, dy, W, H, residual=False, act=False, workspace=None, st
         workspace = lowrank_workspace(x, z, W, H)
     return dsc_lowrank_bwd(x, z, U, dy, torch.empty_like(x), torch.empty_like(z),
                            torch.empty_like(U), workspace, W, H, residual, act, stream)
+
+
+def decode_state(x, W, stream=None):
+    B, T, D = x.shape
+    return dsc_decode_state(x, torch.empty(B, W - 1, D, dtype=x.dtype, device=x.device), stream)
+
+
+def headwise_decode(x, w, state, H, residual=False, act=False, stream=None):
+    return dsc_headwise_decode(x, w, state, torch.empty_like(x), H, residual, act, stream)
+
+
+def lowrank_decode(x, z, U, state, W, H, residual=False, act=False, stream=None):
+    return dsc_lowrank_decode(x, z, U, state, torch.empty_like(x), W, H, residual, act, stream)

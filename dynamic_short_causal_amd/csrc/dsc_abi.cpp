@@ -237,4 +237,64 @@ dsc_status dsc_lowrank_bwd(const void *x, const void *z, const void *U, const vo
   return hip_status(dsc::lowrank_launch(a));
 }
 
+static dsc_status decode_common(const void *x, const void *w, const void *z, const void *U,
+                                void *state, void *y, int64_t B, int64_t D, int W, int H,
+                                int R, dsc_dtype dtype, unsigned flags, void *stream,
+                                bool lowrank) {
+  int V = 0;
+  dsc_status st = lowrank ? lowrank_check(B, 1, D, W, H, R, dtype, flags, &V)
+                          : check_common(B, 1, D, W, H, dtype, flags, &V);
+  if (st != DSC_OK) return st;
+  if (!lowrank && !headwise_h_ok(H, V))
+    return fail(DSC_ERR_UNSUPPORTED,
+                "H=%d: head-wise needs H | %d or H = %d * 2^m with 2^m <= 64", H, V, V);
+  const int es = dtype == DSC_BF16 ? 2 : 4;
+  const int64_t G = D / H;
+  Span s[5] = {span("x", x, B * D, es, false),
+               lowrank ? span("z", z, B * R, es, false) : span("w", w, B * G * W, es, false),
+               span("U", lowrank ? U : nullptr, lowrank ? (int64_t)R * G * W : 0, es, false),
+               span("state", state, B * (W - 1) * D, es, true),
+               span("y", y, B * D, es, true)};
+  if ((st = check_ptrs(s, 5)) != DSC_OK) return st;
+  dsc::DecArgs a{};
+  a.x = x; a.w = w; a.z = z; a.U = U; a.state = state; a.y = y;
+  a.B = B; a.T = 1; a.D = D; a.W = W; a.H = H; a.R = R;
+  a.bf16 = dtype == DSC_BF16;
+  a.residual = (flags & DSC_RESIDUAL) != 0;
+  a.act = (flags & DSC_ACT_SILU) != 0;
+  a.lowrank = lowrank;
+  a.stream = stream;
+  return hip_status(dsc::decode_launch(a));
+}
+
+dsc_status dsc_headwise_decode(const void *x, const void *w, void *state, void *y, int64_t B,
+                               int64_t D, int W, int H, dsc_dtype dtype, unsigned flags,
+                               void *stream) {
+  return decode_common(x, w, nullptr, nullptr, state, y, B, D, W, H, 0, dtype, flags, stream,
+                       false);
+}
+
+dsc_status dsc_lowrank_decode(const void *x, const void *z, const void *U, void *state,
+                              void *y, int64_t B, int64_t D, int W, int H, int R,
+                              dsc_dtype dtype, unsigned flags, void *stream) {
+  return decode_common(x, nullptr, z, U, state, y, B, D, W, H, R, dtype, flags, stream, true);
+}
+
+dsc_status dsc_decode_state(const void *x, void *state, int64_t B, int64_t T, int64_t D, int W,
+                            dsc_dtype dtype, void *stream) {
+  int V = 0;
+  dsc_status st = check_common(B, T, D, W, 1, dtype, 0, &V);
+  if (st != DSC_OK) return st;
+  const int es = dtype == DSC_BF16 ? 2 : 4;
+  Span s[2] = {span("x", x, B * T * D, es, false),
+               span("state", state, B * (W - 1) * D, es, true)};
+  if ((st = check_ptrs(s, 2)) != DSC_OK) return st;
+  dsc::DecArgs a{};
+  a.x = x; a.state = state;
+  a.B = B; a.T = T; a.D = D; a.W = W; a.H = 1;
+  a.bf16 = dtype == DSC_BF16;
+  a.stream = stream;
+  return hip_status(dsc::decode_state_launch(a));
+}
+
 }  // extern "C"

@@ -137,6 +137,38 @@ dsc_status dsc_lowrank_bwd(const void *x, const void *z, const void *U,
                            int64_t T, int64_t D, int W, int H, int R,
                            dsc_dtype dtype, unsigned flags, void *stream);
 
+/*
+ * One-token (decode) steps.  The pages define the convolution over a whole
+ * sequence only; in streaming use, y at the newest token t depends on x_t and
+ * the W-1 inputs before it, which a caller keeps in a state buffer
+ *   state : (B, W-1, D), row j = x_{t-(W-1)+j} (oldest first, zero before the
+ *           start of the sequence; an empty buffer when W == 1).
+ * Each call takes x_t : (B, D) and the filter of token t, writes
+ *   y[b,c] = act(w[b,g(c),0] x_t[b,c] + sum_{k=1}^{W-1} w[b,g(c),k] state[b,W-1-k,c])
+ *            + rho x_t[b,c]
+ * -- row t of the forward above, in the same fp32 arithmetic up to the order
+ * of the sums -- and then advances the state in place by one token
+ * (rows move up by one, x_t becomes the last row; values are copied, not
+ * rounded).  `state` is read and written by the call and must not overlap any
+ * other tensor of it.  B == 0 is legal and empty.  Errors as above.
+ */
+
+/* Head-wise decode step; w : (B, G, W). */
+dsc_status dsc_headwise_decode(const void *x, const void *w, void *state, void *y,
+                               int64_t B, int64_t D, int W, int H, dsc_dtype dtype,
+                               unsigned flags, void *stream);
+
+/* Low-rank decode step; z : (B, R), U : (R, G*W); the filter w = zU is formed
+ * in registers ([gist] bullet Fused Low-Rank Kernel). */
+dsc_status dsc_lowrank_decode(const void *x, const void *z, const void *U, void *state,
+                              void *y, int64_t B, int64_t D, int W, int H, int R,
+                              dsc_dtype dtype, unsigned flags, void *stream);
+
+/* State after a prompt x : (B, T, D): state[b,j] = x[b, T-(W-1)+j], zero where
+ * that index is below 0.  Writes the (B, W-1, D) state only. */
+dsc_status dsc_decode_state(const void *x, void *state, int64_t B, int64_t T, int64_t D,
+                            int W, dsc_dtype dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

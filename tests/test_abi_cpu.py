@@ -128,3 +128,49 @@ def test_workspace_checks(lib):
     assert lrb(lib, ws=A + 4 * BIG + 16) == INVALID          # workspace overlaps dx
     assert lrb(lib, R=70) == UNSUP
     assert lrb(lib, dx=A + 8) == INVALID
+
+
+def hdec(lib, x=A, w=A + BIG, st=A + 2 * BIG, y=A + 3 * BIG, B=2, D=64, W=4, H=1, dt=1, fl=0):
+    p = ctypes.c_void_p
+    return lib.dsc_headwise_decode(p(x), p(w), p(st), p(y), B, D, W, H, dt, fl, None)
+
+
+def ldec(lib, x=A, z=A + BIG, U=A + 2 * BIG, st=A + 3 * BIG, y=A + 4 * BIG, B=2, D=64, W=4, H=1,
+         R=16, dt=1, fl=0):
+    p = ctypes.c_void_p
+    return lib.dsc_lowrank_decode(p(x), p(z), p(U), p(st), p(y), B, D, W, H, R, dt, fl, None)
+
+
+def dstate(lib, x=A, st=A + BIG, B=2, T=8, D=64, W=4, dt=1):
+    p = ctypes.c_void_p
+    return lib.dsc_decode_state(p(x), p(st), B, T, D, W, dt, None)
+
+
+def test_decode_checks(lib):
+    assert hdec(lib, W=9) == UNSUP
+    assert hdec(lib, fl=8) == UNSUP
+    assert hdec(lib, H=3, D=48) == UNSUP
+    assert hdec(lib, D=36) == INVALID                        # not a multiple of 8 (bf16)
+    assert hdec(lib, st=0) == INVALID
+    assert hdec(lib, st=A + 8) == INVALID                    # misaligned
+    assert hdec(lib, st=A + 3 * BIG - 16) == INVALID         # state runs into y
+    assert b"overlaps" in lib.dsc_last_error()
+    assert hdec(lib, y=A + 2 * BIG + 16) == INVALID          # y inside the state
+    assert hdec(lib, B=-1) == INVALID
+    assert ldec(lib, H=16) == UNSUP                          # low-rank needs H | 8
+    assert ldec(lib, R=0) == UNSUP
+    assert ldec(lib, U=0) == INVALID
+    assert ldec(lib, st=A + BIG) == INVALID                  # state overlaps z
+    assert dstate(lib, W=0) == UNSUP
+    assert dstate(lib, T=-1) == INVALID
+    assert dstate(lib, st=A + 16) == INVALID                 # state overlaps x
+    assert dstate(lib, x=0) == INVALID
+
+
+def test_decode_empty(lib):
+    assert hdec(lib, B=0, x=0, w=0, st=0, y=0) == 0
+    assert ldec(lib, B=0, x=0, z=0, st=0, y=0) == 0
+    assert dstate(lib, B=0, x=0, st=0) == 0
+    # W == 1 keeps no state: the pointer is not used, but x, w and y still are
+    assert dstate(lib, W=1, st=0) == 0
+    assert hdec(lib, W=1, st=0, y=0) == INVALID
