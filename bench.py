@@ -205,12 +205,25 @@ def summarize_profiles(d, calls):
     print("\n".join(lines))
 
 
-def decode_bench(dsc, di, torch, dev, stream, iters=200):
-    """One-token steps at serving batches: mean time per step over `iters`
-    back-to-back launches on one stream (HIP events), for head-wise H=16 and
-    low-rank R=16 H=1 at D=6144, W=4, bf16, residual.  Not part of the step."""
+def decode_bench(dsc, di, torch, dev, iters=200):
+    """One-token steps at serving batches, for head-wise H=16 and low-rank R=16
+    H=1 at D=6144, W=4, bf16, residual.  Two timings of `iters` steps in a row:
+    "eager" launches each step from Python (binding and launch cost included),
+    "graph" replays them from one captured HIP graph (device time per step).
+    The state stays the same buffer, as in a serving loop.  Not part of the
+    training step."""
     D, W, R = WORKLOAD["D"], WORKLOAD["W"], WORKLOAD["R"]
     Hh, Hl = WORKLOAD["H_headwise"], WORKLOAD["H_lowrank"]
+    cur = torch.cuda.current_stream()
+
+    def per_step_us(run):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        run()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / iters
+
     out = {}
     for B in (64, 512):
         x = di.randn((B, D), 1.0, 90, "bf16").to(dev)
@@ -220,23 +233,28 @@ def decode_bench(dsc, di, torch, dev, stream, iters=200):
         U = di.randn((R, (D // Hl) * W), 0.125, 94, "bf16").to(dev)
         y = torch.empty_like(x)
         act_bytes = 2 * B * D * (2 + 2 * (W - 1))
-        hw = lambda: dsc.dsc_headwise_decode(x, w, st, y, Hh, True, False, stream)
-        lr = lambda: dsc.dsc_lowrank_decode(x, z, U, st, y, W, Hl, True, False, stream)
+        hw = lambda s: dsc.dsc_headwise_decode(x, w, st, y, Hh, True, False, s)
+        lr = lambda s: dsc.dsc_lowrank_decode(x, z, U, st, y, W, Hl, True, False, s)
         cases = {"headwise": (hw, act_bytes + 2 * B * (D // Hh) * W),
                  "lowrank": (lr, act_bytes + 2 * (B * R + R * (D // Hl) * W))}
         for name, (fn, nbytes) in cases.items():
             for _ in range(10):
-                fn()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(iters):
-                fn()
-            e1.record(stream)
+                fn(cur)
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / iters
-            out[f"{name}_B{B}"] = {"us_per_step": round(us, 2),
-                                   "tokens_per_s": round(B / (us * 1e-6), 1),
-                                   "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            eager = per_step_us(lambda: [fn(cur) for _ in range(iters)])
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cap = torch.cuda.current_stream()
+                for _ in range(iters):
+                    fn(cap)
+            g.replay()
+            torch.cuda.synchronize()
+            graph = per_step_us(g.replay)
+            del g
+            out[f"{name}_B{B}"] = {"eager_us_per_step": round(eager, 2),
+                                   "graph_us_per_step": round(graph, 2),
+                                   "tokens_per_s": round(B / (graph * 1e-6), 1),
+                                   "gbps": round(nbytes / (graph * 1e-6) / 1e9, 1),
                                    "algorithmic_bytes": nbytes}
     return out
 
@@ -355,7 +373,7 @@ def main():
     del src, dst
 
     print("bench: timing decode steps", file=sys.stderr, flush=True)
-    decode = decode_bench(dsc, di, torch, dev, stream)
+    decode = decode_bench(dsc, di, torch, dev)
 
     nbytes = algorithmic_bytes(B, T, D, W, Hh, R, Hl)
     ms_per_step = elapsed / args.steps * 1e3

@@ -11,12 +11,13 @@
 // inference engineering open (wispaper.ai blog "Dynamic Short Convolutions",
 // Limitations); this is the plain streaming form of the same sum.
 //
-// Mapping: one thread per (sequence, 16-byte channel vector).  It reads x_t,
-// its W-1 state rows and the filter taps of its groups (head-wise: a row of w;
-// low-rank: w = z U formed in registers from R rows of U), writes y and rewrites
-// its own slice of the state, so the update in place has a single owner.  A
-// decode step moves a few bytes per channel, far too little to fill matrix
-// cores, so the rank contraction runs on the vector ALUs.
+// Mapping: a thread owns one 16-byte channel vector of one sequence (head-wise)
+// or of a block of sequences (low-rank).  Per sequence it reads x_t, its W-1
+// state rows and the filter taps of its groups (head-wise: a row of w;
+// low-rank: w = z U formed in registers from R rows of U), writes y and
+// rewrites its own slice of the state, so the update in place has a single
+// owner.  A decode step is a few FMAs per byte moved, far too little to fill
+// matrix cores, so the rank contraction runs on the vector ALUs.
 #include "dsc_device.hpp"
 #include "dsc_launch.hpp"
 
@@ -30,33 +31,13 @@ __device__ __forceinline__ float to_f32(E v) {
   else return v;
 }
 
-template <typename E, int W, int GPV, bool LR>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(
-    const E *__restrict__ x, const E *__restrict__ w, const E *__restrict__ z,
-    const E *__restrict__ U, E *__restrict__ state, E *__restrict__ y, int64_t B,
-    int64_t D, int H, int R, int nvec, float rho, int act) {
-  constexpr int V = Vw<E>::n, S = W - 1, HS = V / GPV, NT = GPV * W;
-  const int64_t idx = (int64_t)blockIdx.x * kDecThreads + threadIdx.x;
-  if (idx >= B * nvec) return;
-  const int64_t b = idx / nvec;
-  const int64_t c0 = (idx - b * nvec) * V;
-  const int64_t G = D / H, g0 = c0 / H;  // first filter group of the vector
-  // taps[gi * W + k]: tap k of group g0 + gi
-  float taps[NT];
-  if constexpr (LR) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) taps[j] = 0.f;
-    const int64_t GW = G * W;
-    for (int r = 0; r < R; ++r) {
-      const float zr = to_f32<E>(z[b * R + r]);
-      float u[NT];
-      unpack_row<E, NT>(ld_row<E, NT>(U + r * GW + g0 * W), u);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) taps[j] = fmaf(zr, u[j], taps[j]);
-    }
-  } else {
-    unpack_row<E, NT>(ld_row<E, NT>(w + (b * G + g0) * W), taps);
-  }
+// The state update and output of one sequence b for one channel vector c0.
+template <typename E, int W, int GPV>
+__device__ __forceinline__ void decode_one(const E *__restrict__ x, E *__restrict__ state,
+                                           E *__restrict__ y, int64_t b, int64_t D,
+                                           int64_t c0, const float (&taps)[GPV * W],
+                                           float rho, int act) {
+  constexpr int V = Vw<E>::n, S = W - 1, HS = V / GPV;
   const uint4 xraw = ld16(x + b * D + c0);
   float xt[V];
   unpack<E>(xraw, xt);
@@ -84,6 +65,84 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   if constexpr (S > 0) st16(state + (b * S + S - 1) * D + c0, xraw);
 }
 
+// Head-wise: thread idx owns vector idx % nvec of sequence idx / nvec.
+template <typename E, int W, int GPV>
+__global__ __launch_bounds__(kDecThreads) void decode_hw_kernel(
+    const E *__restrict__ x, const E *__restrict__ w, E *__restrict__ state,
+    E *__restrict__ y, int64_t B, int64_t D, int H, int nvec, float rho, int act) {
+  constexpr int V = Vw<E>::n, NT = GPV * W;
+  const int64_t idx = (int64_t)blockIdx.x * kDecThreads + threadIdx.x;
+  if (idx >= B * nvec) return;
+  const int64_t b = idx / nvec;
+  const int64_t c0 = (idx - b * nvec) * V;
+  const int64_t G = D / H, g0 = c0 / H;  // first filter group of the vector
+  float taps[NT];  // taps[gi * W + k]: tap k of group g0 + gi
+  unpack_row<E, NT>(ld_row<E, NT>(w + (b * G + g0) * W), taps);
+  decode_one<E, W, GPV>(x, state, y, b, D, c0, taps, rho, act);
+}
+
+// Low-rank: thread idx owns vector idx % nvec of the NB sequences from
+// NB * (idx / nvec).  Each row chunk of U it loads serves all NB sequences,
+// which divides the (cache) reads of U by NB; U is R * G * W elements and is
+// read once per sequence block.
+template <typename E, int W, int GPV, int NB>
+__global__ __launch_bounds__(kDecThreads) void decode_lr_kernel(
+    const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U,
+    E *__restrict__ state, E *__restrict__ y, int64_t B, int64_t D, int H, int R, int nvec,
+    float rho, int act) {
+  constexpr int V = Vw<E>::n, NT = GPV * W;
+  const int64_t nsb = (B + NB - 1) / NB;
+  const int64_t idx = (int64_t)blockIdx.x * kDecThreads + threadIdx.x;
+  if (idx >= nsb * nvec) return;
+  const int64_t sb = idx / nvec;
+  const int64_t c0 = (idx - sb * nvec) * V;
+  const int64_t G = D / H, g0 = c0 / H, GW = G * W, b0 = sb * NB;
+  float taps[NB][NT];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) taps[i][j] = 0.f;
+  // rows of z past B read row B-1; their taps are discarded below
+  int64_t zrow[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) zrow[i] = (b0 + i < B ? b0 + i : B - 1) * R;
+  // UNR rows of U in flight at once
+  constexpr int UNR = NT <= 32 ? 4 : 2;
+  int r = 0;
+  for (; r + UNR <= R; r += UNR) {
+    RowBits<E, NT> ub[UNR];
+    float zr[UNR][NB];
+#pragma unroll
+    for (int q = 0; q < UNR; ++q) {
+      ub[q] = ld_row<E, NT>(U + (r + q) * GW + g0 * W);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) zr[q][i] = to_f32<E>(z[zrow[i] + r + q]);
+    }
+#pragma unroll
+    for (int q = 0; q < UNR; ++q) {
+      float u[NT];
+      unpack_row<E, NT>(ub[q], u);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) taps[i][j] = fmaf(zr[q][i], u[j], taps[i][j]);
+    }
+  }
+  for (; r < R; ++r) {
+    float u[NT];
+    unpack_row<E, NT>(ld_row<E, NT>(U + r * GW + g0 * W), u);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const float zr = to_f32<E>(z[zrow[i] + r]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) taps[i][j] = fmaf(zr, u[j], taps[i][j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    if (b0 + i < B) decode_one<E, W, GPV>(x, state, y, b0 + i, D, c0, taps[i], rho, act);
+}
+
 // state[b, j] = x[b, T-(W-1)+j] of a prompt (B, T, D), zero before its start
 template <typename E>
 __global__ __launch_bounds__(kDecThreads) void decode_state_kernel(
@@ -100,23 +159,36 @@ __global__ __launch_bounds__(kDecThreads) void decode_state_kernel(
   st16(state + row * D + c0, v);
 }
 
+template <typename E, int W, int GPV, int NB>
+static hipError_t launch_dec_lr(const DecArgs &a, int nvec, float rho) {
+  const int64_t n = (a.B + NB - 1) / NB * nvec;
+  const unsigned grid = (unsigned)((n + kDecThreads - 1) / kDecThreads);
+  hipLaunchKernelGGL((decode_lr_kernel<E, W, GPV, NB>), dim3(grid), dim3(kDecThreads), 0,
+                     (hipStream_t)a.stream, (const E *)a.x, (const E *)a.z, (const E *)a.U,
+                     (E *)a.state, (E *)a.y, a.B, a.D, a.H, a.R, nvec, rho, a.act ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Threads of one launch at which the low-rank step blocks sequences: four
+// 256-thread workgroups per compute unit before blocking, so the grid still
+// covers the chip after it.
+constexpr int64_t kDecBlockFrom = 4 * 256 * kDecThreads;
+
 template <typename E, int W, int GPV>
 static hipError_t launch_dec(const DecArgs &a) {
-  constexpr int V = Vw<E>::n;
+  constexpr int V = Vw<E>::n, NT = GPV * W;
   const int nvec = (int)(a.D / V);
-  const int64_t n = a.B * nvec;
-  if (n == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((n + kDecThreads - 1) / kDecThreads);
+  if (a.B == 0) return hipSuccess;
   const float rho = a.residual ? 1.f : 0.f;
-  hipStream_t s = (hipStream_t)a.stream;
-  if (a.lowrank)
-    hipLaunchKernelGGL((decode_kernel<E, W, GPV, true>), dim3(grid), dim3(kDecThreads), 0, s,
-                       (const E *)a.x, (const E *)nullptr, (const E *)a.z, (const E *)a.U,
-                       (E *)a.state, (E *)a.y, a.B, a.D, a.H, a.R, nvec, rho, a.act ? 1 : 0);
-  else
-    hipLaunchKernelGGL((decode_kernel<E, W, GPV, false>), dim3(grid), dim3(kDecThreads), 0, s,
-                       (const E *)a.x, (const E *)a.w, (const E *)nullptr, (const E *)nullptr,
-                       (E *)a.state, (E *)a.y, a.B, a.D, a.H, 0, nvec, rho, a.act ? 1 : 0);
+  if (a.lowrank) {
+    if (a.B * nvec < kDecBlockFrom) return launch_dec_lr<E, W, GPV, 1>(a, nvec, rho);
+    return launch_dec_lr<E, W, GPV, (NT <= 32 ? 4 : 2)>(a, nvec, rho);
+  }
+  const int64_t n = a.B * nvec;
+  const unsigned grid = (unsigned)((n + kDecThreads - 1) / kDecThreads);
+  hipLaunchKernelGGL((decode_hw_kernel<E, W, GPV>), dim3(grid), dim3(kDecThreads), 0,
+                     (hipStream_t)a.stream, (const E *)a.x, (const E *)a.w, (E *)a.state,
+                     (E *)a.y, a.B, a.D, a.H, nvec, rho, a.act ? 1 : 0);
   return hipGetLastError();
 }
 

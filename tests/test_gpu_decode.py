@@ -117,3 +117,70 @@ def test_serving_batch(dsc, orc, lowrank, D, H):
     """One step at a serving batch of 64 sequences and the workloads' widths,
     from the state of a 100-token prompt."""
     roll(dsc, orc, lowrank, 64, 101, D, 4, H, torch.bfloat16, True, H == 8, 7000 + H, T0=100)
+
+
+@pytest.mark.parametrize("lowrank", [False, True], ids=["headwise", "lowrank"])
+def test_graph_replay(dsc, orc, lowrank):
+    """Decode steps captured in one HIP graph give, on every replay, the bits
+    of the same steps launched eagerly (the kernels queue no memset)."""
+    B, T, D, W, H, R = 4, 6, 512, 4, 1 if lowrank else 8, 16
+    G = D // H
+    dev = gu.dev()
+    xs = [di.randn((B, D), 1.0, 7100 + t, "bf16").to(dev) for t in range(T)]
+    if lowrank:
+        zs = [di.randn((B, R), 1.0, 7200 + t, "bf16").to(dev) for t in range(T)]
+        U = di.randn((R, G * W), 0.125, 7300, "bf16").to(dev)
+    else:
+        ws = [di.randn((B, G, W), 0.5, 7200 + t, "bf16").to(dev) for t in range(T)]
+    init = di.randn((B, W - 1, D), 1.0, 7400, "bf16").to(dev)
+    state = init.clone()
+    ys = [torch.empty_like(xs[0]) for _ in range(T)]
+
+    def steps(s):
+        for t in range(T):
+            if lowrank:
+                dsc.dsc_lowrank_decode(xs[t], zs[t], U, state, ys[t], W, H, True, True, s)
+            else:
+                dsc.dsc_headwise_decode(xs[t], ws[t], state, ys[t], H, True, True, s)
+
+    steps(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref_y = [y.clone() for y in ys]
+    ref_state = state.clone()
+    # the eager steps agree with the oracle from the same initial state
+    st = gu.f64(init)
+    for t in range(T):
+        if lowrank:
+            yo, st = orc.lowrank_decode(gu.f64(xs[t]), gu.f64(zs[t]), gu.f64(U), st, W, H, True,
+                                        True)
+        else:
+            yo, st = orc.headwise_decode(gu.f64(xs[t]), gu.f64(ws[t]), st, H, True, True)
+        gu.check(f"eager y[{t}]", ref_y[t], yo, torch.bfloat16, "y")
+    assert np.array_equal(gu.f64(ref_state), st)
+
+    state.copy_(init)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        steps(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(3):
+        state.copy_(init)
+        for y in ys:
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t in range(T):
+            assert torch.equal(ys[t], ref_y[t]), f"replay {rep} y[{t}]"
+        assert torch.equal(state, ref_state), f"replay {rep} state"
+
+
+@pytest.mark.parametrize("B,D,W,dtype,R", [(343, 6144, 4, torch.bfloat16, 16),
+                                           (259, 4096, 4, torch.float32, 7),
+                                           (343, 6144, 8, torch.bfloat16, 3)])
+def test_lowrank_sequence_blocks(dsc, orc, B, D, W, dtype, R):
+    """Batches large enough that each low-rank thread serves a block of
+    sequences (a ragged last block here), with R a multiple of, above and
+    below the rows of U loaded together."""
+    roll(dsc, orc, True, B, 5, D, W, 1, dtype, True, False, 7500 + R, T0=3, R=R)
