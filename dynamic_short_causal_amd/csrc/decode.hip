@@ -19,7 +19,7 @@
 // owner.  A decode step is a few FMAs per byte moved, far too little to fill
 // matrix cores, so the rank contraction runs on the vector ALUs.
 #include "dsc_device.hpp"
-#include "dsc_launch.hpp"
+#include "decode_launch.hpp"
 
 namespace dsc {
 

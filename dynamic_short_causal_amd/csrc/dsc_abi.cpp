@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include "dsc_launch.hpp"
+#include "decode_launch.hpp"
 
 namespace {
 

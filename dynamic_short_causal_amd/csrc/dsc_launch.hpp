@@ -26,17 +26,6 @@ struct LrArgs {
   void *stream;
 };
 
-// One-token steps (decode.hip): head-wise uses w (B, G, W); low-rank uses
-// z (B, R) and U (R, G*W).  dsc_decode_state reads x as a prompt (B, T, D).
-struct DecArgs {
-  const void *x, *w, *z, *U;
-  void *state, *y;
-  int64_t B, T, D;
-  int W, H, R;
-  bool bf16, residual, act, lowrank;
-  void *stream;
-};
-
 // Tiling of the low-rank backward and the workspace it implies.  Shared by
 // the workspace query and the launcher so the two always agree.
 struct LrBwdPlan {
@@ -92,8 +81,6 @@ inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int 
 }
 
 hipError_t headwise_launch(const HwArgs &a);
-hipError_t decode_launch(const DecArgs &a);
-hipError_t decode_state_launch(const DecArgs &a);
 hipError_t lowrank_launch(const LrArgs &a);
 
 }  // namespace dsc
