@@ -50,6 +50,9 @@ def _declare(lib):
         "oracle_lowrank_decode": [_dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _int, _int,
                                   _int, _int, _int],
         "oracle_decode_state": [_dp, _dp, _i64, _i64, _i64, _int],
+        "oracle_static_fwd": [_dp, _dp, _dp, _i64, _i64, _i64, _int, _int, _int, _int],
+        "oracle_static_bwd": [_dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _int, _int, _int,
+                              _int],
         "oracle_num_threads": [],
         "oracle_set_num_threads": [_int],
     }
@@ -236,6 +239,28 @@ class Oracle:
         st = np.empty((B, W - 1, D))
         self.lib.oracle_decode_state(_p(x), _p(st), B, T, D, W)
         return st
+
+    # ---- static short convolution (one filter for all positions) ----------
+    def static_fwd(self, x, w, H, residual=False, act=False):
+        """x (B,T,D), w (G,W) -> y (B,T,D)."""
+        x, w = _c(x), _c(w)
+        B, T, D = x.shape
+        assert w.shape[0] == D // H
+        y = np.empty_like(x)
+        self.lib.oracle_static_fwd(_p(x), _p(w), _p(y), B, T, D, w.shape[1], H,
+                                   int(residual), int(act))
+        return y
+
+    def static_bwd(self, x, w, dy, H, residual=False, act=False):
+        """-> (dx (B,T,D), dw (G,W))."""
+        x, w, dy = _c(x), _c(w), _c(dy)
+        B, T, D = x.shape
+        assert w.shape[0] == D // H and dy.shape == x.shape
+        dx = np.empty_like(x)
+        dw = np.empty_like(w)
+        self.lib.oracle_static_bwd(_p(x), _p(w), _p(dy), _p(dx), _p(dw), B, T, D, w.shape[1],
+                                   H, int(residual), int(act))
+        return dx, dw
 
 
 _DEFAULT = None

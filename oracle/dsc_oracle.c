@@ -474,3 +474,74 @@ void oracle_decode_state(const double *x, double *state, int64_t B, int64_t T,
         state[(b * S + j) * D + c] = t >= 0 ? x[IDX3(b, t, c, T, D)] : 0.0;
     }
 }
+
+/*
+ * Static short convolution: the same causal sum with one fixed filter per
+ * group for every sequence and position.  [wisp] Methodology > 1.
+ * Mathematical Intuition writes it as y_t = sum_k w_k x_{t-k} beside the
+ * dynamic form; [thread] describes it as a depthwise-separable causal
+ * convolution of small width, and [gist] Prestaties names such kernels as the
+ * latency yardstick for the dynamic ones.  Tying over H channels, zero taps
+ * before the sequence start, residual and activation follow the dynamic path.
+ * Layouts: x, y, dy, dx (B, T, D); w, dw (G, W).
+ */
+static double static_s(const double *x, const double *w, int64_t T, int64_t D,
+                       int W, int H, int64_t b, int64_t t, int64_t c) {
+  const double *wg = w + (c / H) * W;
+  double s = 0.0;
+  for (int k = 0; k < W && t - k >= 0; ++k) s += wg[k] * x[IDX3(b, t - k, c, T, D)];
+  return s;
+}
+
+void oracle_static_fwd(const double *x, const double *w, double *y, int64_t B,
+                       int64_t T, int64_t D, int W, int H, int residual, int act) {
+  int64_t N = B * T;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    int64_t b = n / T, t = n % T;
+    for (int64_t c = 0; c < D; ++c)
+      y[n * D + c] = act_fn(static_s(x, w, T, D, W, H, b, t, c), act) +
+                     (residual ? x[n * D + c] : 0.0);
+  }
+}
+
+/*
+ * Its derivative.  With ds = dy * act'(s):
+ *   dx[b,tau,c] = sum_{k: tau+k<T} w[g(c),k] * ds[b,tau+k,c] + rho * dy[b,tau,c]
+ *   dw[g,k]     = sum_b sum_{t>=k} sum_{c in g} ds[b,t,c] * x[b,t-k,c]
+ * dw sums over every sequence and position, because the one filter serves them
+ * all; each dw element is one sequential sum in the order (b, t, c).
+ */
+static double static_ds(const double *x, const double *w, const double *dy,
+                        int64_t T, int64_t D, int W, int H, int act, int64_t b,
+                        int64_t t, int64_t c) {
+  double g = dy[IDX3(b, t, c, T, D)];
+  return act ? g * act_grad(static_s(x, w, T, D, W, H, b, t, c), act) : g;
+}
+
+void oracle_static_bwd(const double *x, const double *w, const double *dy, double *dx,
+                       double *dw, int64_t B, int64_t T, int64_t D, int W, int H,
+                       int residual, int act) {
+  int64_t G = D / H, N = B * T;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    int64_t b = n / T, tau = n % T;
+    for (int64_t c = 0; c < D; ++c) {
+      double acc = 0.0;
+      for (int k = 0; k < W && tau + k < T; ++k)
+        acc += w[(c / H) * W + k] * static_ds(x, w, dy, T, D, W, H, act, b, tau + k, c);
+      dx[n * D + c] = acc + (residual ? dy[n * D + c] : 0.0);
+    }
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < G * W; ++j) {
+    int64_t g = j / W;
+    int k = (int)(j % W);
+    double acc = 0.0;
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t t = k; t < T; ++t)
+        for (int64_t c = g * H; c < (g + 1) * H; ++c)
+          acc += static_ds(x, w, dy, T, D, W, H, act, b, t, c) * x[IDX3(b, t - k, c, T, D)];
+    dw[j] = acc;
+  }
+}

@@ -378,8 +378,75 @@ def pin_decode_rolls_forward(orc):
             yt, _ = orc.lowrank_decode(x[:, T0], z[:, T0], U, st, W, H, residual=res, act=act)
             _close(yt, yl[:, T0], what=f"low-rank decode after a {T0}-token prompt")
 
+# ---------------------------------------------------------------- static filters
+def _conv1d_static(x, w, H, residual, act, dy):
+    """y and the gradients of <y, dy> through torch's depthwise conv1d (fp64):
+    the (G, W) filter repeated over its H channels, taps flipped (conv1d's last
+    weight meets the newest input), W-1 zeros of left padding."""
+    B, T, D = x.shape
+    W = w.shape[1]
+    xt = torch.tensor(x, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    kern = wt.repeat_interleave(H, dim=0).flip(-1)[:, None, :]       # (D, 1, W)
+    s = F.conv1d(xt.transpose(1, 2), kern, padding=W - 1, groups=D)[:, :, :T].transpose(1, 2)
+    y = F.silu(s) if act else s
+    if residual:
+        y = y + xt
+    y.backward(torch.tensor(dy))
+    return y.detach().numpy(), xt.grad.numpy(), wt.grad.numpy()
+
+
+def pin_static_is_conv1d(orc):
+    """The static forward and both gradients equal torch conv1d + autograd."""
+    rng = _rng(40)
+    for (B, T, D, W, H) in [(2, 13, 8, 4, 1), (3, 5, 12, 3, 4), (1, 3, 8, 6, 2),
+                            (2, 9, 16, 1, 16)]:
+        x, dy = _rand(rng, B, T, D), _rand(rng, B, T, D)
+        w = _rand(rng, D // H, W, std=0.5)
+        for res, act in ((False, False), (True, False), (False, True), (True, True)):
+            y, dx, dw = _conv1d_static(x, w, H, res, act, dy)
+            _close(orc.static_fwd(x, w, H, res, act), y, what=f"static y {B,T,D,W,H}")
+            dxo, dwo = orc.static_bwd(x, w, dy, H, res, act)
+            _close(dxo, dx, what=f"static dx {B,T,D,W,H}")
+            _close(dwo, dw, rtol=1e-11, atol=1e-11, what=f"static dw {B,T,D,W,H}")
+
+
+def pin_static_is_broadcast_dynamic(orc):
+    """A static filter is a dynamic one repeated over (b, t): same y and dx,
+    and the static dw is the dynamic dw summed over every sequence and token."""
+    rng = _rng(41)
+    for (B, T, D, W, H) in [(2, 11, 8, 4, 2), (3, 4, 6, 5, 3)]:
+        x, dy = _rand(rng, B, T, D), _rand(rng, B, T, D)
+        w = _rand(rng, D // H, W, std=0.5)
+        wb = np.broadcast_to(w, (B, T) + w.shape).copy()
+        for res, act in ((True, False), (False, True)):
+            _close(orc.static_fwd(x, w, H, res, act), orc.headwise_fwd(x, wb, H, res, act),
+                   what="static vs broadcast y")
+            dxs, dws = orc.static_bwd(x, w, dy, H, res, act)
+            dxh, dwh = orc.headwise_bwd(x, wb, dy, H, res, act)
+            _close(dxs, dxh, what="static vs broadcast dx")
+            _close(dws, dwh.sum(axis=(0, 1)), rtol=1e-11, atol=1e-11,
+                   what="static dw vs summed dynamic dw")
+
+
+def pin_static_finite_differences(orc):
+    """Central differences of L = <y, dy> for dx and dw, T < W included."""
+    rng = _rng(42)
+    for (B, T, D, W, H) in [(2, 6, 6, 3, 3), (1, 2, 4, 4, 1)]:
+        x, dy = _rand(rng, B, T, D), _rand(rng, B, T, D)
+        w = _rand(rng, D // H, W, std=0.5)
+        for res, act in ((False, False), (True, True)):
+            def Lx(xx): return np.sum(orc.static_fwd(xx, w, H, res, act) * dy)
+            def Lw(ww): return np.sum(orc.static_fwd(x, ww, H, res, act) * dy)
+            dx, dw = orc.static_bwd(x, w, dy, H, res, act)
+            _close(dx, _fd(Lx, x), rtol=1e-7, atol=1e-7, what="fd static dx")
+            _close(dw, _fd(Lw, w), rtol=1e-7, atol=1e-7, what="fd static dw")
+
+
 ALL_PINS = [pin_handworked, pin_width_one_is_scale, pin_silu_values,
             pin_static_filter_is_conv1d, pin_causality, pin_linearity,
             pin_residual_is_tap0_shift, pin_tying_is_repeat, pin_lowrank_is_headwise,
             pin_adjoint, pin_euler, pin_finite_differences, pin_torch_autograd,
-            pin_sampled_match_full, pin_decode_handworked, pin_decode_rolls_forward]
+            pin_sampled_match_full, pin_decode_handworked, pin_decode_rolls_forward,
+            pin_static_is_conv1d, pin_static_is_broadcast_dynamic,
+            pin_static_finite_differences]

@@ -45,6 +45,12 @@ MUTANTS = {
     "decode_no_shift": ("state_out[(b * S + j) * D + c] = state_in[(b * S + j + 1) * D + c];",
                         "state_out[(b * S + j) * D + c] = state_in[(b * S + j) * D + c];"),
     "decode_state_offset": ("int64_t t = T - S + j;", "int64_t t = T - S + j - 1;"),
+    "static_reversed_taps": ("for (int k = 0; k < W && t - k >= 0; ++k) s += wg[k] * x",
+                             "for (int k = 0; k < W && t - k >= 0; ++k) s += wg[W - 1 - k] * x"),
+    "static_dw_one_sequence": ("    for (int64_t b = 0; b < B; ++b)\n      for (int64_t t = k; t < T; ++t)",
+                               "    for (int64_t b = 0; b < 1; ++b)\n      for (int64_t t = k; t < T; ++t)"),
+    "static_dx_unshifted_ds": ("acc += w[(c / H) * W + k] * static_ds(x, w, dy, T, D, W, H, act, b, tau + k, c);",
+                               "acc += w[(c / H) * W + k] * static_ds(x, w, dy, T, D, W, H, act, b, tau, c);"),
     "residual_twice": ("y[n * D + c] = act_fn(s, act) + (residual ? x[n * D + c] : 0.0);\n    }\n  }\n}",
                        "y[n * D + c] = act_fn(s, act) + (residual ? 2.0 * x[n * D + c] : 0.0);\n    }\n  }\n}"),
 }
