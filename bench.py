@@ -205,6 +205,49 @@ def summarize_profiles(d, calls):
     print("\n".join(lines))
 
 
+def static_bench(dsc, di, torch, dev, steps, per_kernel_ms):
+    """The static-filter comparator at the step's shape: per-channel filters
+    (H=1, the depthwise form), bf16, residual, forward and backward, each op on
+    its own copy of the inputs, mean of `steps` event-timed launches.  Set
+    beside the dynamic ops it answers how much the per-token filters cost over
+    a fixed filter.  Not part of the step."""
+    B, T, D, W = WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"]
+    N, es = B * T, 2
+    stream = torch.cuda.current_stream()
+    x = di.randn((B, T, D), 1.0, 95, "bf16").to(dev)
+    w = di.randn((D, W), 0.5, 96, "bf16").to(dev)
+    dy = di.randn((B, T, D), 1.0, 97, "bf16").to(dev)
+    xb = x.clone()
+    y, dx, dw = torch.empty_like(x), torch.empty_like(x), torch.empty_like(w)
+    ws = dsc.static_workspace(x, W, 1)
+    ops = {"static_fwd": (lambda: dsc.dsc_static_fwd(x, w, y, 1, True, False, stream),
+                          es * (2 * N * D + D * W)),
+           "static_bwd": (lambda: dsc.dsc_static_bwd(xb, w, dy, dx, dw, ws, 1, True, False,
+                                                     stream),
+                          es * (3 * N * D + 2 * D * W))}
+    out = {}
+    for name, (fn, nbytes) in ops.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+        out[name] = {"ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "algorithmic_bytes": nbytes}
+    t_static = out["static_fwd"]["ms"] + out["static_bwd"]["ms"]
+    out["tokens_per_s"] = round(N / (t_static * 1e-3), 1)
+    for v in ("headwise", "lowrank"):
+        t_dyn = per_kernel_ms[f"{v}_fwd"] + per_kernel_ms[f"{v}_bwd"]
+        out[f"{v}_time_over_static"] = round(t_dyn / t_static, 3)
+    return out
+
+
 def decode_bench(dsc, di, torch, dev, iters=200):
     """One-token steps at serving batches, for head-wise H=16 and low-rank R=16
     H=1 at D=6144, W=4, bf16, residual.  Two timings of `iters` steps in a row:
@@ -374,6 +417,8 @@ def main():
 
     print("bench: timing decode steps", file=sys.stderr, flush=True)
     decode = decode_bench(dsc, di, torch, dev)
+    print("bench: timing the static-filter comparator", file=sys.stderr, flush=True)
+    static = static_bench(dsc, di, torch, dev, args.steps, per_kernel_ms)
 
     nbytes = algorithmic_bytes(B, T, D, W, Hh, R, Hl)
     ms_per_step = elapsed / args.steps * 1e3
@@ -417,6 +462,7 @@ def main():
         "kernels": kernels,
         "variants": variants,
         "decode": decode,
+        "static_comparator": static,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -25,7 +25,8 @@ DSC_RESIDUAL, DSC_ACT_SILU = 1, 2
 EXPORTS = ("dsc_version", "dsc_status_string", "dsc_last_error", "dsc_headwise_fwd",
            "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd_workspace_bytes",
            "dsc_lowrank_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
-           "dsc_decode_state")
+           "dsc_decode_state", "dsc_static_fwd", "dsc_static_bwd_workspace_bytes",
+           "dsc_static_bwd")
 
 
 class DscError(RuntimeError):
@@ -55,9 +56,14 @@ def _load():
     lib.dsc_headwise_decode.argtypes = [vp, vp, vp, vp, i64, i64, ci, ci, ci, cu, vp]
     lib.dsc_lowrank_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, ci, cu, vp]
     lib.dsc_decode_state.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
+    lib.dsc_static_fwd.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, cu, vp]
+    lib.dsc_static_bwd_workspace_bytes.argtypes = [i64, i64, i64, ci, ci, ci]
+    lib.dsc_static_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.dsc_static_bwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, ci,
+                                   ci, ci, cu, vp]
     for name in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd",
                  "dsc_lowrank_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
-                 "dsc_decode_state"):
+                 "dsc_decode_state", "dsc_static_fwd", "dsc_static_bwd"):
         getattr(lib, name).restype = ci
     return lib
 
@@ -198,6 +204,35 @@ def dsc_decode_state(x, state, stream=None):
     return state
 
 
+def dsc_static_fwd(x, w, y, H, residual=False, act=False, stream=None):
+    """Static filter w (G, W) for every sequence and token."""
+    B, T, D = x.shape
+    W = w.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("w", w, (D // H, W)), ("y", y, (B, T, D))):
+        _need(t, n, s, x.dtype)
+    _check(LIB.dsc_static_fwd(_ptr(x), _ptr(w), _ptr(y), B, T, D, W, H, _dtype(x),
+                              _flags(residual, act), _stream(stream)))
+    return y
+
+
+def dsc_static_bwd_workspace_bytes(B, T, D, W, H, dtype):
+    d = DSC_BF16 if dtype == torch.bfloat16 else DSC_F32
+    return int(LIB.dsc_static_bwd_workspace_bytes(B, T, D, W, H, d))
+
+
+def dsc_static_bwd(x, w, dy, dx, dw, workspace, H, residual=False, act=False, stream=None):
+    B, T, D = x.shape
+    W = w.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("w", w, (D // H, W)), ("dy", dy, (B, T, D)),
+                    ("dx", dx, (B, T, D)), ("dw", dw, (D // H, W))):
+        _need(t, n, s, x.dtype)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.dsc_static_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(workspace),
+                              nbytes, B, T, D, W, H, _dtype(x), _flags(residual, act),
+                              _stream(stream)))
+    return dx, dw
+
+
 # --------------------------------------------------------------- allocating forms
 def headwise_fwd(x, w, H, residual=False, act=False, stream=None):
     return dsc_headwise_fwd(x, w, torch.empty_like(x), H, residual, act, stream)
@@ -236,3 +271,20 @@ def headwise_decode(x, w, state, H, residual=False, act=False, stream=None):
 
 def lowrank_decode(x, z, U, state, W, H, residual=False, act=False, stream=None):
     return dsc_lowrank_decode(x, z, U, state, torch.empty_like(x), W, H, residual, act, stream)
+
+
+def static_fwd(x, w, H, residual=False, act=False, stream=None):
+    return dsc_static_fwd(x, w, torch.empty_like(x), H, residual, act, stream)
+
+
+def static_workspace(x, W, H):
+    B, T, D = x.shape
+    n = dsc_static_bwd_workspace_bytes(B, T, D, W, H, x.dtype)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+
+
+def static_bwd(x, w, dy, H, residual=False, act=False, workspace=None, stream=None):
+    if workspace is None:
+        workspace = static_workspace(x, w.shape[-1], H)
+    return dsc_static_bwd(x, w, dy, torch.empty_like(x), torch.empty_like(w), workspace, H,
+                          residual, act, stream)

@@ -19,8 +19,9 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsc.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dsc_abi.cpp", "headwise.hip", "decode.hip", "lowrank.hip", "lowrank_fwd_bf16.hip",
-           "lowrank_bwd_bf16.hip", "lowrank_fwd_f32.hip", "lowrank_bwd_f32.hip"]
+SOURCES = ["dsc_abi.cpp", "headwise.hip", "decode.hip", "static.hip", "lowrank.hip",
+           "lowrank_fwd_bf16.hip", "lowrank_bwd_bf16.hip", "lowrank_fwd_f32.hip",
+           "lowrank_bwd_f32.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

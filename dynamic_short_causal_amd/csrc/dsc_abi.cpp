@@ -10,6 +10,7 @@
 
 #include "dsc_launch.hpp"
 #include "decode_launch.hpp"
+#include "static_launch.hpp"
 
 namespace {
 
@@ -296,6 +297,75 @@ dsc_status dsc_decode_state(const void *x, void *state, int64_t B, int64_t T, in
   a.bf16 = dtype == DSC_BF16;
   a.stream = stream;
   return hip_status(dsc::decode_state_launch(a));
+}
+
+static dsc_status static_check(int64_t B, int64_t T, int64_t D, int W, int H, dsc_dtype dtype,
+                               unsigned flags) {
+  int V = 0;
+  dsc_status st = check_common(B, T, D, W, H, dtype, flags, &V);
+  if (st != DSC_OK) return st;
+  if (!headwise_h_ok(H, V))
+    return fail(DSC_ERR_UNSUPPORTED,
+                "H=%d: the static path needs H | %d or H = %d * 2^m with 2^m <= 64", H, V, V);
+  return DSC_OK;
+}
+
+static dsc::StArgs static_args(int64_t B, int64_t T, int64_t D, int W, int H, dsc_dtype dtype,
+                               unsigned flags, void *stream, bool bwd) {
+  dsc::StArgs a{};
+  a.B = B; a.T = T; a.D = D; a.W = W; a.H = H;
+  a.bf16 = dtype == DSC_BF16;
+  a.residual = (flags & DSC_RESIDUAL) != 0;
+  a.act = (flags & DSC_ACT_SILU) != 0;
+  a.bwd = bwd;
+  a.stream = stream;
+  return a;
+}
+
+dsc_status dsc_static_fwd(const void *x, const void *w, void *y, int64_t B, int64_t T,
+                          int64_t D, int W, int H, dsc_dtype dtype, unsigned flags,
+                          void *stream) {
+  dsc_status st = static_check(B, T, D, W, H, dtype, flags);
+  if (st != DSC_OK) return st;
+  const int es = dtype == DSC_BF16 ? 2 : 4;
+  const int64_t n_act = B * T * D, n_w = (D / H) * W;
+  Span s[3] = {span("x", x, n_act, es, false), span("w", w, n_w, es, false),
+               span("y", y, n_act, es, true)};
+  if ((st = check_ptrs(s, 3)) != DSC_OK) return st;
+  dsc::StArgs a = static_args(B, T, D, W, H, dtype, flags, stream, false);
+  a.x = x; a.w = w; a.y = y;
+  return hip_status(dsc::static_launch(a));
+}
+
+size_t dsc_static_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int W, int H,
+                                      dsc_dtype dtype) {
+  if (static_check(B, T, D, W, H, dtype, 0) != DSC_OK) return 0;
+  if (B == 0 || T == 0) return 0;
+  return dsc::st_plan(B, T, D, W, H).bytes;
+}
+
+dsc_status dsc_static_bwd(const void *x, const void *w, const void *dy, void *dx, void *dw,
+                          void *workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                          int64_t D, int W, int H, dsc_dtype dtype, unsigned flags,
+                          void *stream) {
+  dsc_status st = static_check(B, T, D, W, H, dtype, flags);
+  if (st != DSC_OK) return st;
+  const int es = dtype == DSC_BF16 ? 2 : 4;
+  const int64_t n_act = B * T * D, n_w = (D / H) * W;
+  const size_t need = (B == 0 || T == 0) ? 0 : dsc::st_plan(B, T, D, W, H).bytes;
+  if (need > 0 && workspace_bytes < need)
+    return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed",
+                workspace_bytes, need);
+  if (need > 0 && workspace == nullptr)
+    return fail(DSC_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  Span s[6] = {span("x", x, n_act, es, false),  span("w", w, n_w, es, false),
+               span("dy", dy, n_act, es, false), span("dx", dx, n_act, es, true),
+               span("dw", dw, n_w, es, true),
+               span("workspace", workspace, (int64_t)need, 1, true)};
+  if ((st = check_ptrs(s, 6)) != DSC_OK) return st;
+  dsc::StArgs a = static_args(B, T, D, W, H, dtype, flags, stream, true);
+  a.x = x; a.w = w; a.dy = dy; a.dx = dx; a.dw = dw; a.ws = workspace;
+  return hip_status(dsc::static_launch(a));
 }
 
 }  // extern "C"

@@ -49,7 +49,8 @@
  *                        vector width times a power of two up to 64; low-rank:
  *                        H divides the vector width);
  *   DSC_ERR_WORKSPACE    workspace smaller than dsc_lowrank_bwd_workspace_bytes
- *                        (or NULL while that is non-zero);
+ *                        (dsc_static_bwd_workspace_bytes for dsc_static_bwd),
+ *                        or NULL while that is non-zero;
  *   DSC_ERR_HIP          a HIP launch error (the message holds HIP's text).
  * B == 0 or T == 0 is legal and empty; the low-rank backward then still
  * writes dU = 0.
@@ -168,6 +169,38 @@ dsc_status dsc_lowrank_decode(const void *x, const void *z, const void *U, void 
  * that index is below 0.  Writes the (B, W-1, D) state only. */
 dsc_status dsc_decode_state(const void *x, void *state, int64_t B, int64_t T, int64_t D,
                             int W, dsc_dtype dtype, void *stream);
+
+/*
+ * Static short convolution: the same causal sum with one filter per group
+ * for every sequence and position,
+ *   y[b,t,c] = act(sum_{k<W} w[g(c),k] * x[b,t-k,c]) + rho * x[b,t,c],
+ * w : (G, W).  It is the fixed-filter form the pages contrast with the dynamic
+ * one ([wisp] Methodology, 1. Mathematical Intuition) and the kind of kernel
+ * they measure the dynamic kernels against ([gist] Efficiente
+ * Trainingsimplementatie, bullet Prestaties).  Tying factors, flags, layouts
+ * of x, y, dy, dx and errors are those of the head-wise calls.
+ */
+dsc_status dsc_static_fwd(const void *x, const void *w, void *y, int64_t B, int64_t T,
+                          int64_t D, int W, int H, dsc_dtype dtype, unsigned flags,
+                          void *stream);
+
+/* Bytes of workspace dsc_static_bwd needs: fp32 partial sums of dw, one row
+ * of G*W per sequence and 512-token span.  0 for an empty call or for
+ * arguments dsc_static_bwd would reject. */
+size_t dsc_static_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int W, int H,
+                                      dsc_dtype dtype);
+
+/*
+ * Static backward: dx (B,T,D) as in dsc_headwise_bwd with the fixed filter, and
+ *   dw[g,k] = sum_b sum_{t>=k} sum_{c : g(c)=g} ds[b,t,c] * x[b,t-k,c]   (G, W)
+ * summed over every sequence and token; partial sums go to `workspace` and a
+ * second kernel on the same stream adds them in a fixed order.  An empty call
+ * (B == 0 or T == 0) writes dw = 0.
+ */
+dsc_status dsc_static_bwd(const void *x, const void *w, const void *dy, void *dx, void *dw,
+                          void *workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                          int64_t D, int W, int H, dsc_dtype dtype, unsigned flags,
+                          void *stream);
 
 #ifdef __cplusplus
 }

@@ -16,9 +16,9 @@ HEADER = os.path.join(ROOT, "include", "dsc.h")
 
 @pytest.fixture(scope="module")
 def lib():
-    from dynamic_short_causal_amd import build as b
-    if not os.path.exists(b.LIB):
-        b.build()
+    import __graft_entry__ as ge
+    if not os.path.exists(os.path.join(ROOT, "dynamic_short_causal_amd", "libdsc.so")):
+        ge._library_builder().build()
     import dynamic_short_causal_amd as d
     return d.LIB
 
@@ -35,6 +35,27 @@ def test_exports_every_declared_symbol(lib):
     assert names and set(names) == set(d.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_binding_signatures_match_header(lib):
+    """Every binding declares as many arguments as the header, with 64-bit
+    types where the header has int64_t or size_t."""
+    import ctypes as ct
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, params in re.findall(r"\b(dsc_[a-z_0-9]+)\s*\(([^)]*)\)\s*;", text):
+        params = [q.strip() for q in params.split(",") if q.strip() and q.strip() != "void"]
+        fn = getattr(lib, name)
+        got = fn.argtypes or []
+        assert len(got) == len(params), (name, len(got), len(params))
+        for q, t in zip(params, got):
+            if q.startswith("int64_t"):
+                assert t is ct.c_int64, (name, q)
+            elif q.startswith("size_t"):
+                assert t is ct.c_size_t, (name, q)
+            elif "*" in q:
+                assert t is ct.c_void_p, (name, q)
+        if re.search(r"size_t\s+" + name + r"\s*\(", text):
+            assert fn.restype is ct.c_size_t, name
 
 
 def test_status_strings(lib):
@@ -174,3 +195,34 @@ def test_decode_empty(lib):
     # W == 1 keeps no state: the pointer is not used, but x, w and y still are
     assert dstate(lib, W=1, st=0) == 0
     assert hdec(lib, W=1, st=0, y=0) == INVALID
+
+
+def sfw(lib, x=A, w=A + BIG, y=A + 2 * BIG, B=1, T=8, D=64, W=4, H=1, dt=1, fl=0):
+    p = ctypes.c_void_p
+    return lib.dsc_static_fwd(p(x), p(w), p(y), B, T, D, W, H, dt, fl, None)
+
+
+def sbw(lib, ws=A + 5 * BIG, wsb=None, B=1, T=8, D=64, W=4, H=1, dt=1, fl=0, dw=A + 4 * BIG):
+    p = ctypes.c_void_p
+    if wsb is None:
+        wsb = lib.dsc_static_bwd_workspace_bytes(B, T, D, W, H, dt)
+    return lib.dsc_static_bwd(p(A), p(A + BIG), p(A + 2 * BIG), p(A + 3 * BIG), p(dw), p(ws),
+                              wsb, B, T, D, W, H, dt, fl, None)
+
+
+def test_static_checks(lib):
+    assert sfw(lib, W=9) == UNSUP
+    assert sfw(lib, H=3, D=48) == UNSUP
+    assert sfw(lib, D=36) == INVALID
+    assert sfw(lib, w=0) == INVALID
+    assert sfw(lib, y=A + BIG + 16) == INVALID               # y overlaps w
+    n = lib.dsc_static_bwd_workspace_bytes(1, 8, 64, 4, 1, 1)
+    assert n == 64 * 4 * 4                                   # one 512-token span: G*W fp32
+    assert lib.dsc_static_bwd_workspace_bytes(8, 2048, 6144, 4, 1, 1) == 8 * 4 * 6144 * 4 * 4
+    assert lib.dsc_static_bwd_workspace_bytes(1, 8, 64, 9, 1, 1) == 0
+    assert lib.dsc_static_bwd_workspace_bytes(0, 8, 64, 4, 1, 1) == 0
+    assert sbw(lib, wsb=n - 1) == WS
+    assert sbw(lib, ws=0) == WS
+    assert sbw(lib, ws=A + 3 * BIG + 16) == INVALID          # workspace overlaps dx
+    assert sbw(lib, dw=A + BIG) == INVALID                   # dw overlaps w
+    assert sbw(lib, fl=16) == UNSUP
