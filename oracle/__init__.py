@@ -23,6 +23,7 @@ _i64 = ctypes.c_int64
 _int = ctypes.c_int
 _dp = ctypes.POINTER(ctypes.c_double)
 _lp = ctypes.POINTER(ctypes.c_int64)
+_ip = ctypes.POINTER(ctypes.c_int32)
 
 
 def _declare(lib):
@@ -50,6 +51,14 @@ def _declare(lib):
         "oracle_lowrank_decode": [_dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _int, _int,
                                   _int, _int, _int],
         "oracle_decode_state": [_dp, _dp, _i64, _i64, _i64, _int],
+        "oracle_headwise_fwd_vl": [_dp, _dp, _ip, _dp, _i64, _i64, _i64, _int, _int, _int,
+                                   _int],
+        "oracle_headwise_bwd_vl": [_dp, _dp, _ip, _dp, _dp, _dp, _i64, _i64, _i64, _int, _int,
+                                   _int, _int],
+        "oracle_lowrank_fwd_vl": [_dp, _dp, _dp, _ip, _dp, _i64, _i64, _i64, _int, _int, _int,
+                                  _int, _int],
+        "oracle_lowrank_bwd_vl": [_dp, _dp, _dp, _ip, _dp, _dp, _dp, _dp, _i64, _i64, _i64,
+                                  _int, _int, _int, _int, _int],
         "oracle_static_fwd": [_dp, _dp, _dp, _i64, _i64, _i64, _int, _int, _int, _int],
         "oracle_static_bwd": [_dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _int, _int, _int,
                               _int],
@@ -261,6 +270,51 @@ class Oracle:
         self.lib.oracle_static_bwd(_p(x), _p(w), _p(dy), _p(dx), _p(dw), B, T, D, w.shape[1],
                                    H, int(residual), int(act))
         return dx, dw
+
+    # ---- packed variable-length sequences ---------------------------------
+    @staticmethod
+    def _pos(pos, B, T):
+        p = np.ascontiguousarray(pos, dtype=np.int32)
+        assert p.shape == (B, T)
+        return p, p.ctypes.data_as(_ip)
+
+    def headwise_fwd_vl(self, x, w, pos, H, residual=False, act=False):
+        """As headwise_fwd, tap k of token t only when k <= pos[b, t]."""
+        x, w = _c(x), _c(w)
+        B, T, D = x.shape
+        p, pp = self._pos(pos, B, T)
+        y = np.empty_like(x)
+        self.lib.oracle_headwise_fwd_vl(_p(x), _p(w), pp, _p(y), B, T, D, w.shape[-1], H,
+                                        int(residual), int(act))
+        return y
+
+    def headwise_bwd_vl(self, x, w, pos, dy, H, residual=False, act=False):
+        x, w, dy = _c(x), _c(w), _c(dy)
+        B, T, D = x.shape
+        p, pp = self._pos(pos, B, T)
+        dx, dw = np.empty_like(x), np.empty_like(w)
+        self.lib.oracle_headwise_bwd_vl(_p(x), _p(w), pp, _p(dy), _p(dx), _p(dw), B, T, D,
+                                        w.shape[-1], H, int(residual), int(act))
+        return dx, dw
+
+    def lowrank_fwd_vl(self, x, z, U, pos, W, H, residual=False, act=False):
+        x, z, U = _c(x), _c(z), _c(U)
+        B, T, D = x.shape
+        p, pp = self._pos(pos, B, T)
+        y = np.empty_like(x)
+        self.lib.oracle_lowrank_fwd_vl(_p(x), _p(z), _p(U), pp, _p(y), B, T, D, W, H,
+                                       z.shape[-1], int(residual), int(act))
+        return y
+
+    def lowrank_bwd_vl(self, x, z, U, pos, dy, W, H, residual=False, act=False):
+        x, z, U, dy = _c(x), _c(z), _c(U), _c(dy)
+        B, T, D = x.shape
+        p, pp = self._pos(pos, B, T)
+        dx, dz, dU = np.empty_like(x), np.empty_like(z), np.empty_like(U)
+        self.lib.oracle_lowrank_bwd_vl(_p(x), _p(z), _p(U), pp, _p(dy), _p(dx), _p(dz),
+                                       _p(dU), B, T, D, W, H, z.shape[-1], int(residual),
+                                       int(act))
+        return dx, dz, dU
 
 
 _DEFAULT = None

@@ -545,3 +545,111 @@ void oracle_static_bwd(const double *x, const double *w, const double *dy, doubl
     dw[j] = acc;
   }
 }
+
+/*
+ * Packed variable-length sequences.  The pages train on whole rows; packing
+ * several documents into one row (each starting fresh) is a training-side
+ * convention they do not discuss.  The reading taken: pos[b,t] (int32) is
+ * token t's index inside its document, 0 at a document start, and tap k of
+ * token t exists only when k <= pos[b,t], so no tap reaches into the previous
+ * document.  With pos[b,t] = t this is the dense operation above.  Masked taps
+ * contribute nothing and receive zero gradient.
+ * Layouts as above, plus pos (B, T).
+ */
+static double vl_s(const double *x, const double *w, const int32_t *pos, int64_t T,
+                   int64_t D, int64_t G, int W, int H, int64_t n, int64_t c) {
+  int64_t t = n % T, g = c / H;
+  double s = 0.0;
+  for (int k = 0; k < W; ++k)
+    if (k <= pos[n] && t - k >= 0) s += w[(n * G + g) * W + k] * x[(n - k) * D + c];
+  return s;
+}
+
+static double vl_ds(const double *x, const double *w, const int32_t *pos, const double *dy,
+                    int64_t T, int64_t D, int64_t G, int W, int H, int act, int64_t n,
+                    int64_t c) {
+  double gy = dy[n * D + c];
+  return act ? gy * act_grad(vl_s(x, w, pos, T, D, G, W, H, n, c), act) : gy;
+}
+
+void oracle_headwise_fwd_vl(const double *x, const double *w, const int32_t *pos, double *y,
+                            int64_t B, int64_t T, int64_t D, int W, int H, int residual,
+                            int act) {
+  int64_t G = D / H, N = B * T;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t c = 0; c < D; ++c)
+      y[n * D + c] = act_fn(vl_s(x, w, pos, T, D, G, W, H, n, c), act) +
+                     (residual ? x[n * D + c] : 0.0);
+}
+
+/* dx[b,tau,c] = sum_{k : tau+k < T, k <= pos[b,tau+k]} w[b,tau+k,g,k] ds[b,tau+k,c]
+ *               + rho dy[b,tau,c];
+ * dw[b,t,g,k] = sum_{c in g} ds[b,t,c] x[b,t-k,c] when tap k of t exists, else 0. */
+void oracle_headwise_bwd_vl(const double *x, const double *w, const int32_t *pos,
+                            const double *dy, double *dx, double *dw, int64_t B, int64_t T,
+                            int64_t D, int W, int H, int residual, int act) {
+  int64_t G = D / H, N = B * T;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    int64_t tau = n % T;
+    for (int64_t c = 0; c < D; ++c) {
+      double acc = 0.0;
+      for (int k = 0; k < W && tau + k < T; ++k) {
+        int64_t m = n + k;
+        if (k <= pos[m])
+          acc += w[(m * G + c / H) * W + k] * vl_ds(x, w, pos, dy, T, D, G, W, H, act, m, c);
+      }
+      dx[n * D + c] = acc + (residual ? dy[n * D + c] : 0.0);
+    }
+    for (int64_t g = 0; g < G; ++g)
+      for (int k = 0; k < W; ++k) {
+        double acc = 0.0;
+        if (k <= pos[n] && tau - k >= 0)
+          for (int64_t c = g * H; c < (g + 1) * H; ++c)
+            acc += vl_ds(x, w, pos, dy, T, D, G, W, H, act, n, c) * x[(n - k) * D + c];
+        dw[(n * G + g) * W + k] = acc;
+      }
+  }
+}
+
+/* Low-rank forms: w = zU materialised, then the masked head-wise pass;
+ * dz = dw U^T and dU = z^T dw with the masked dw. */
+void oracle_lowrank_fwd_vl(const double *x, const double *z, const double *U,
+                           const int32_t *pos, double *y, int64_t B, int64_t T, int64_t D,
+                           int W, int H, int R, int residual, int act) {
+  int64_t G = D / H;
+  double *w = (double *)malloc(sizeof(double) * (size_t)(B * T * G * W));
+  if (!w) return;
+  oracle_lowrank_w(z, U, w, B, T, G, W, R);
+  oracle_headwise_fwd_vl(x, w, pos, y, B, T, D, W, H, residual, act);
+  free(w);
+}
+
+void oracle_lowrank_bwd_vl(const double *x, const double *z, const double *U,
+                           const int32_t *pos, const double *dy, double *dx, double *dz,
+                           double *dU, int64_t B, int64_t T, int64_t D, int W, int H, int R,
+                           int residual, int act) {
+  int64_t G = D / H, N = B * T, GW = G * W;
+  double *w = (double *)malloc(sizeof(double) * (size_t)(N * GW));
+  double *gw = (double *)malloc(sizeof(double) * (size_t)(N * GW));
+  if (!w || !gw) { free(w); free(gw); return; }
+  oracle_lowrank_w(z, U, w, B, T, G, W, R);
+  oracle_headwise_bwd_vl(x, w, pos, dy, dx, gw, B, T, D, W, H, residual, act);
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int r = 0; r < R; ++r) {
+      double s = 0.0;
+      for (int64_t j = 0; j < GW; ++j) s += gw[n * GW + j] * U[(int64_t)r * GW + j];
+      dz[n * R + r] = s;
+    }
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < GW; ++j)
+    for (int r = 0; r < R; ++r) {
+      double s = 0.0;
+      for (int64_t n = 0; n < N; ++n) s += z[n * R + r] * gw[n * GW + j];
+      dU[(int64_t)r * GW + j] = s;
+    }
+  free(w);
+  free(gw);
+}

@@ -442,6 +442,99 @@ def pin_static_finite_differences(orc):
             _close(dx, _fd(Lx, x), rtol=1e-7, atol=1e-7, what="fd static dx")
             _close(dw, _fd(Lw, w), rtol=1e-7, atol=1e-7, what="fd static dw")
 
+# ---------------------------------------------------------------- packed documents
+def _packing(rng, B, T, max_docs=4):
+    """pos[b, t] for rows packed with documents of random lengths (>= 1)."""
+    pos = np.zeros((B, T), dtype=np.int32)
+    spans = []
+    for b in range(B):
+        cuts = sorted(rng.choice(np.arange(1, T), size=min(max_docs - 1, T - 1),
+                                 replace=False)) if T > 1 else []
+        edges = [0] + list(cuts) + [T]
+        row = []
+        for s0, e0 in zip(edges[:-1], edges[1:]):
+            pos[b, s0:e0] = np.arange(e0 - s0)
+            row.append((s0, e0))
+        spans.append(row)
+    return pos, spans
+
+
+def pin_varlen_one_document_is_dense(orc):
+    """pos[b, t] = t (one document per row) gives the dense results."""
+    rng = _rng(50)
+    B, T, D, W, H, R = 2, 9, 8, 4, 2, 3
+    G = D // H
+    x, dy = _rand(rng, B, T, D), _rand(rng, B, T, D)
+    w = _rand(rng, B, T, G, W, std=0.5)
+    z, U = _rand(rng, B, T, R), _rand(rng, R, G * W, std=0.5)
+    pos = np.tile(np.arange(T, dtype=np.int32), (B, 1))
+    for res, act in ((True, False), (False, True)):
+        _close(orc.headwise_fwd_vl(x, w, pos, H, res, act), orc.headwise_fwd(x, w, H, res, act),
+               what="vl dense y")
+        for a, b in zip(orc.headwise_bwd_vl(x, w, pos, dy, H, res, act),
+                        orc.headwise_bwd(x, w, dy, H, res, act)):
+            _close(a, b, what="vl dense head-wise grads")
+        _close(orc.lowrank_fwd_vl(x, z, U, pos, W, H, res, act),
+               orc.lowrank_fwd(x, z, U, W, H, res, act), what="vl dense low-rank y")
+        for a, b in zip(orc.lowrank_bwd_vl(x, z, U, pos, dy, W, H, res, act),
+                        orc.lowrank_bwd(x, z, U, dy, W, H, res, act)):
+            _close(a, b, what="vl dense low-rank grads")
+
+
+def pin_varlen_documents_are_independent(orc):
+    """A packed row gives, document by document, what the dense operation gives
+    on that document alone; dU is the sum of the documents' dU."""
+    rng = _rng(51)
+    for (B, T, D, W, H, R) in [(2, 17, 8, 4, 2, 3), (3, 12, 6, 3, 3, 2), (1, 9, 4, 5, 1, 4)]:
+        G = D // H
+        x, dy = _rand(rng, B, T, D), _rand(rng, B, T, D)
+        w = _rand(rng, B, T, G, W, std=0.5)
+        z, U = _rand(rng, B, T, R), _rand(rng, R, G * W, std=0.5)
+        pos, spans = _packing(rng, B, T)
+        for res, act in ((True, False), (False, True), (True, True)):
+            y = orc.headwise_fwd_vl(x, w, pos, H, res, act)
+            dx, dw = orc.headwise_bwd_vl(x, w, pos, dy, H, res, act)
+            yl = orc.lowrank_fwd_vl(x, z, U, pos, W, H, res, act)
+            dxl, dz, dU = orc.lowrank_bwd_vl(x, z, U, pos, dy, W, H, res, act)
+            dU_sum = np.zeros_like(U)
+            for b in range(B):
+                for s0, e0 in spans[b]:
+                    sl = (slice(b, b + 1), slice(s0, e0))
+                    xs, ws, dys, zs = x[sl], w[sl], dy[sl], z[sl]
+                    _close(y[sl], orc.headwise_fwd(xs, ws, H, res, act), what="vl doc y")
+                    ddx, ddw = orc.headwise_bwd(xs, ws, dys, H, res, act)
+                    _close(dx[sl], ddx, what="vl doc dx")
+                    _close(dw[sl], ddw, what="vl doc dw")
+                    _close(yl[sl], orc.lowrank_fwd(xs, zs, U, W, H, res, act),
+                           what="vl doc low-rank y")
+                    ldx, ldz, ldU = orc.lowrank_bwd(xs, zs, U, dys, W, H, res, act)
+                    _close(dxl[sl], ldx, what="vl doc low-rank dx")
+                    _close(dz[sl], ldz, what="vl doc dz")
+                    dU_sum += ldU
+            _close(dU, dU_sum, rtol=1e-11, atol=1e-11, what="vl dU over documents")
+
+
+def pin_varlen_finite_differences(orc):
+    """Central differences of <y, dy> through packed rows."""
+    rng = _rng(52)
+    B, T, D, W, H, R = 2, 7, 4, 3, 2, 2
+    G = D // H
+    x, dy = _rand(rng, B, T, D), _rand(rng, B, T, D)
+    w = _rand(rng, B, T, G, W, std=0.5)
+    z, U = _rand(rng, B, T, R), _rand(rng, R, G * W, std=0.5)
+    pos, _ = _packing(rng, B, T, max_docs=3)
+    for res, act in ((False, False), (True, True)):
+        dx, dw = orc.headwise_bwd_vl(x, w, pos, dy, H, res, act)
+        _close(dx, _fd(lambda a: np.sum(orc.headwise_fwd_vl(a, w, pos, H, res, act) * dy), x),
+               rtol=1e-7, atol=1e-7, what="fd vl dx")
+        _close(dw, _fd(lambda a: np.sum(orc.headwise_fwd_vl(x, a, pos, H, res, act) * dy), w),
+               rtol=1e-7, atol=1e-7, what="fd vl dw")
+        _, dz, dU = orc.lowrank_bwd_vl(x, z, U, pos, dy, W, H, res, act)
+        _close(dz, _fd(lambda a: np.sum(orc.lowrank_fwd_vl(x, a, U, pos, W, H, res, act) * dy),
+                       z), rtol=1e-7, atol=1e-7, what="fd vl dz")
+        _close(dU, _fd(lambda a: np.sum(orc.lowrank_fwd_vl(x, z, a, pos, W, H, res, act) * dy),
+                       U), rtol=1e-7, atol=1e-7, what="fd vl dU")
+
 
 ALL_PINS = [pin_handworked, pin_width_one_is_scale, pin_silu_values,
             pin_static_filter_is_conv1d, pin_causality, pin_linearity,
@@ -449,4 +542,5 @@ ALL_PINS = [pin_handworked, pin_width_one_is_scale, pin_silu_values,
             pin_adjoint, pin_euler, pin_finite_differences, pin_torch_autograd,
             pin_sampled_match_full, pin_decode_handworked, pin_decode_rolls_forward,
             pin_static_is_conv1d, pin_static_is_broadcast_dynamic,
-            pin_static_finite_differences]
+            pin_static_finite_differences, pin_varlen_one_document_is_dense,
+            pin_varlen_documents_are_independent, pin_varlen_finite_differences]

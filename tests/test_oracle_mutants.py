@@ -51,6 +51,10 @@ MUTANTS = {
                                "    for (int64_t b = 0; b < 1; ++b)\n      for (int64_t t = k; t < T; ++t)"),
     "static_dx_unshifted_ds": ("acc += w[(c / H) * W + k] * static_ds(x, w, dy, T, D, W, H, act, b, tau + k, c);",
                                "acc += w[(c / H) * W + k] * static_ds(x, w, dy, T, D, W, H, act, b, tau, c);"),
+    "varlen_tap_off_by_one": ("if (k <= pos[n] && t - k >= 0) s += w[(n * G + g) * W + k]",
+                              "if (k < pos[n] && t - k >= 0) s += w[(n * G + g) * W + k]"),
+    "varlen_dx_mask_own_pos": ("        if (k <= pos[m])\n", "        if (k <= pos[n])\n"),
+    "varlen_dw_unmasked": ("        if (k <= pos[n] && tau - k >= 0)\n", "        if (tau - k >= 0)\n"),
     "residual_twice": ("y[n * D + c] = act_fn(s, act) + (residual ? x[n * D + c] : 0.0);\n    }\n  }\n}",
                        "y[n * D + c] = act_fn(s, act) + (residual ? 2.0 * x[n * D + c] : 0.0);\n    }\n  }\n}"),
 }
