@@ -26,7 +26,8 @@ EXPORTS = ("dsc_version", "dsc_status_string", "dsc_last_error", "dsc_headwise_f
            "dsc_headwise_bwd", "dsc_lowrank_fwd", "dsc_lowrank_bwd_workspace_bytes",
            "dsc_lowrank_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
            "dsc_decode_state", "dsc_static_fwd", "dsc_static_bwd_workspace_bytes",
-           "dsc_static_bwd")
+           "dsc_static_bwd", "dsc_headwise_fwd_varlen", "dsc_headwise_bwd_varlen",
+           "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen")
 
 
 class DscError(RuntimeError):
@@ -61,9 +62,18 @@ def _load():
     lib.dsc_static_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.dsc_static_bwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, ci,
                                    ci, ci, cu, vp]
+    lib.dsc_headwise_fwd_varlen.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, cu, vp]
+    lib.dsc_headwise_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, ci,
+                                            cu, vp]
+    lib.dsc_lowrank_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, ci,
+                                           cu, vp]
+    lib.dsc_lowrank_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                           i64, i64, i64, ci, ci, ci, ci, cu, vp]
     for name in ("dsc_headwise_fwd", "dsc_headwise_bwd", "dsc_lowrank_fwd",
                  "dsc_lowrank_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
-                 "dsc_decode_state", "dsc_static_fwd", "dsc_static_bwd"):
+                 "dsc_decode_state", "dsc_static_fwd", "dsc_static_bwd",
+                 "dsc_headwise_fwd_varlen", "dsc_headwise_bwd_varlen",
+                 "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen"):
         getattr(lib, name).restype = ci
     return lib
 
@@ -233,6 +243,69 @@ def dsc_static_bwd(x, w, dy, dx, dw, workspace, H, residual=False, act=False, st
     return dx, dw
 
 
+def _need_pos(pos, B, T):
+    if pos.dtype != torch.int32:
+        raise TypeError(f"pos has dtype {pos.dtype}, expected torch.int32")
+    if tuple(pos.shape) != (B, T):
+        raise ValueError(f"pos has shape {tuple(pos.shape)}, expected {(B, T)}")
+    if not pos.is_contiguous() or not pos.is_cuda:
+        raise ValueError("pos must be a contiguous device tensor")
+
+
+def dsc_headwise_fwd_varlen(x, w, pos, y, H, residual=False, act=False, stream=None):
+    """Packed rows: pos (B, T) int32 holds each token's index in its document."""
+    B, T, D = x.shape
+    W = w.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("w", w, (B, T, D // H, W)), ("y", y, (B, T, D))):
+        _need(t, n, s, x.dtype)
+    _need_pos(pos, B, T)
+    _check(LIB.dsc_headwise_fwd_varlen(_ptr(x), _ptr(w), _ptr(pos), _ptr(y), B, T, D, W, H,
+                                       _dtype(x), _flags(residual, act), _stream(stream)))
+    return y
+
+
+def dsc_headwise_bwd_varlen(x, w, pos, dy, dx, dw, H, residual=False, act=False, stream=None):
+    B, T, D = x.shape
+    W = w.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("w", w, (B, T, D // H, W)), ("dy", dy, (B, T, D)),
+                    ("dx", dx, (B, T, D)), ("dw", dw, (B, T, D // H, W))):
+        _need(t, n, s, x.dtype)
+    _need_pos(pos, B, T)
+    _check(LIB.dsc_headwise_bwd_varlen(_ptr(x), _ptr(w), _ptr(pos), _ptr(dy), _ptr(dx),
+                                       _ptr(dw), B, T, D, W, H, _dtype(x), _flags(residual, act),
+                                       _stream(stream)))
+    return dx, dw
+
+
+def dsc_lowrank_fwd_varlen(x, z, U, pos, y, W, H, residual=False, act=False, stream=None):
+    B, T, D = x.shape
+    R = z.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("z", z, (B, T, R)), ("U", U, (R, (D // H) * W)),
+                    ("y", y, (B, T, D))):
+        _need(t, n, s, x.dtype)
+    _need_pos(pos, B, T)
+    _check(LIB.dsc_lowrank_fwd_varlen(_ptr(x), _ptr(z), _ptr(U), _ptr(pos), _ptr(y), B, T, D,
+                                      W, H, R, _dtype(x), _flags(residual, act),
+                                      _stream(stream)))
+    return y
+
+
+def dsc_lowrank_bwd_varlen(x, z, U, pos, dy, dx, dz, dU, workspace, W, H, residual=False,
+                           act=False, stream=None):
+    B, T, D = x.shape
+    R = z.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("z", z, (B, T, R)), ("U", U, (R, (D // H) * W)),
+                    ("dy", dy, (B, T, D)), ("dx", dx, (B, T, D)), ("dz", dz, (B, T, R)),
+                    ("dU", dU, (R, (D // H) * W))):
+        _need(t, n, s, x.dtype)
+    _need_pos(pos, B, T)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.dsc_lowrank_bwd_varlen(_ptr(x), _ptr(z), _ptr(U), _ptr(pos), _ptr(dy), _ptr(dx),
+                                      _ptr(dz), _ptr(dU), _ptr(workspace), nbytes, B, T, D, W,
+                                      H, R, _dtype(x), _flags(residual, act), _stream(stream)))
+    return dx, dz, dU
+
+
 # --------------------------------------------------------------- allocating forms
 def headwise_fwd(x, w, H, residual=False, act=False, stream=None):
     return dsc_headwise_fwd(x, w, torch.empty_like(x), H, residual, act, stream)
@@ -288,3 +361,24 @@ def static_bwd(x, w, dy, H, residual=False, act=False, workspace=None, stream=No
         workspace = static_workspace(x, w.shape[-1], H)
     return dsc_static_bwd(x, w, dy, torch.empty_like(x), torch.empty_like(w), workspace, H,
                           residual, act, stream)
+
+
+def headwise_fwd_varlen(x, w, pos, H, residual=False, act=False, stream=None):
+    return dsc_headwise_fwd_varlen(x, w, pos, torch.empty_like(x), H, residual, act, stream)
+
+
+def headwise_bwd_varlen(x, w, pos, dy, H, residual=False, act=False, stream=None):
+    return dsc_headwise_bwd_varlen(x, w, pos, dy, torch.empty_like(x), torch.empty_like(w), H,
+                                   residual, act, stream)
+
+
+def lowrank_fwd_varlen(x, z, U, pos, W, H, residual=False, act=False, stream=None):
+    return dsc_lowrank_fwd_varlen(x, z, U, pos, torch.empty_like(x), W, H, residual, act, stream)
+
+
+def lowrank_bwd_varlen(x, z, U, pos, dy, W, H, residual=False, act=False, workspace=None,
+                       stream=None):
+    if workspace is None:
+        workspace = lowrank_workspace(x, z, W, H)
+    return dsc_lowrank_bwd_varlen(x, z, U, pos, dy, torch.empty_like(x), torch.empty_like(z),
+                                  torch.empty_like(U), workspace, W, H, residual, act, stream)

@@ -21,7 +21,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["dsc_abi.cpp", "headwise.hip", "decode.hip", "static.hip", "lowrank.hip",
            "lowrank_fwd_bf16.hip", "lowrank_bwd_bf16.hip", "lowrank_fwd_f32.hip",
-           "lowrank_bwd_f32.hip"]
+           "lowrank_bwd_f32.hip", "lowrank_fwd_bf16_vl.hip", "lowrank_bwd_bf16_vl.hip",
+           "lowrank_fwd_f32_vl.hip", "lowrank_bwd_f32_vl.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -120,10 +120,10 @@ const char *dsc_status_string(dsc_status s) {
 
 const char *dsc_last_error(void) { return g_err; }
 
-static dsc_status headwise_common(const void *x, const void *w, const void *dy, void *y,
-                                  void *dx, void *dw, int64_t B, int64_t T, int64_t D, int W,
-                                  int H, dsc_dtype dtype, unsigned flags, void *stream,
-                                  bool bwd) {
+static dsc_status headwise_common(const void *x, const void *w, const void *dy,
+                                  const int32_t *pos, bool varlen, void *y, void *dx, void *dw,
+                                  int64_t B, int64_t T, int64_t D, int W, int H,
+                                  dsc_dtype dtype, unsigned flags, void *stream, bool bwd) {
   int V = 0;
   dsc_status st = check_common(B, T, D, W, H, dtype, flags, &V);
   if (st != DSC_OK) return st;
@@ -132,18 +132,20 @@ static dsc_status headwise_common(const void *x, const void *w, const void *dy, 
                 "H=%d: head-wise needs H | %d or H = %d * 2^m with 2^m <= 64", H, V, V);
   const int es = dtype == DSC_BF16 ? 2 : 4;
   const int64_t n_act = B * T * D, n_w = B * T * (D / H) * W;
+  const Span sp = span("pos", pos, varlen ? B * T : 0, 4, false);
   if (!bwd) {
-    Span s[3] = {span("x", x, n_act, es, false), span("w", w, n_w, es, false),
-                 span("y", y, n_act, es, true)};
-    if ((st = check_ptrs(s, 3)) != DSC_OK) return st;
+    Span s[4] = {span("x", x, n_act, es, false), span("w", w, n_w, es, false),
+                 span("y", y, n_act, es, true), sp};
+    if ((st = check_ptrs(s, 4)) != DSC_OK) return st;
   } else {
-    Span s[5] = {span("x", x, n_act, es, false), span("w", w, n_w, es, false),
+    Span s[6] = {span("x", x, n_act, es, false), span("w", w, n_w, es, false),
                  span("dy", dy, n_act, es, false), span("dx", dx, n_act, es, true),
-                 span("dw", dw, n_w, es, true)};
-    if ((st = check_ptrs(s, 5)) != DSC_OK) return st;
+                 span("dw", dw, n_w, es, true), sp};
+    if ((st = check_ptrs(s, 6)) != DSC_OK) return st;
   }
   dsc::HwArgs a{};
   a.x = x; a.w = w; a.dy = dy; a.y = y; a.dx = dx; a.dw = dw;
+  a.pos = varlen ? pos : nullptr;
   a.B = B; a.T = T; a.D = D; a.W = W; a.H = H;
   a.bf16 = dtype == DSC_BF16;
   a.residual = (flags & DSC_RESIDUAL) != 0;
@@ -156,15 +158,30 @@ static dsc_status headwise_common(const void *x, const void *w, const void *dy, 
 dsc_status dsc_headwise_fwd(const void *x, const void *w, void *y, int64_t B, int64_t T,
                             int64_t D, int W, int H, dsc_dtype dtype, unsigned flags,
                             void *stream) {
-  return headwise_common(x, w, nullptr, y, nullptr, nullptr, B, T, D, W, H, dtype, flags,
-                         stream, false);
+  return headwise_common(x, w, nullptr, nullptr, false, y, nullptr, nullptr, B, T, D, W, H,
+                         dtype, flags, stream, false);
 }
 
 dsc_status dsc_headwise_bwd(const void *x, const void *w, const void *dy, void *dx, void *dw,
                             int64_t B, int64_t T, int64_t D, int W, int H, dsc_dtype dtype,
                             unsigned flags, void *stream) {
-  return headwise_common(x, w, dy, nullptr, dx, dw, B, T, D, W, H, dtype, flags, stream,
-                         true);
+  return headwise_common(x, w, dy, nullptr, false, nullptr, dx, dw, B, T, D, W, H, dtype, flags,
+                         stream, true);
+}
+
+dsc_status dsc_headwise_fwd_varlen(const void *x, const void *w, const int32_t *pos, void *y,
+                                   int64_t B, int64_t T, int64_t D, int W, int H,
+                                   dsc_dtype dtype, unsigned flags, void *stream) {
+  return headwise_common(x, w, nullptr, pos, true, y, nullptr, nullptr, B, T, D, W, H, dtype,
+                         flags, stream, false);
+}
+
+dsc_status dsc_headwise_bwd_varlen(const void *x, const void *w, const int32_t *pos,
+                                   const void *dy, void *dx, void *dw, int64_t B, int64_t T,
+                                   int64_t D, int W, int H, dsc_dtype dtype, unsigned flags,
+                                   void *stream) {
+  return headwise_common(x, w, dy, pos, true, nullptr, dx, dw, B, T, D, W, H, dtype, flags,
+                         stream, true);
 }
 
 static dsc_status lowrank_check(int64_t B, int64_t T, int64_t D, int W, int H, int R,
@@ -177,20 +194,22 @@ static dsc_status lowrank_check(int64_t B, int64_t T, int64_t D, int W, int H, i
   return DSC_OK;
 }
 
-dsc_status dsc_lowrank_fwd(const void *x, const void *z, const void *U, void *y, int64_t B,
-                           int64_t T, int64_t D, int W, int H, int R, dsc_dtype dtype,
-                           unsigned flags, void *stream) {
+static dsc_status lowrank_fwd_common(const void *x, const void *z, const void *U,
+                                     const int32_t *pos, bool varlen, void *y, int64_t B,
+                                     int64_t T, int64_t D, int W, int H, int R, dsc_dtype dtype,
+                                     unsigned flags, void *stream) {
   int V = 0;
   dsc_status st = lowrank_check(B, T, D, W, H, R, dtype, flags, &V);
   if (st != DSC_OK) return st;
   const int es = dtype == DSC_BF16 ? 2 : 4;
   const int64_t n_act = B * T * D;
-  Span s[4] = {span("x", x, n_act, es, false), span("z", z, B * T * R, es, false),
+  Span s[5] = {span("x", x, n_act, es, false), span("z", z, B * T * R, es, false),
                span("U", U, (int64_t)R * (D / H) * W, es, false),
-               span("y", y, n_act, es, true)};
-  if ((st = check_ptrs(s, 4)) != DSC_OK) return st;
+               span("y", y, n_act, es, true), span("pos", pos, varlen ? B * T : 0, 4, false)};
+  if ((st = check_ptrs(s, 5)) != DSC_OK) return st;
   dsc::LrArgs a{};
   a.x = x; a.z = z; a.U = U; a.y = y;
+  a.pos = varlen ? pos : nullptr;
   a.B = B; a.T = T; a.D = D; a.W = W; a.H = H; a.R = R;
   a.bf16 = dtype == DSC_BF16;
   a.residual = (flags & DSC_RESIDUAL) != 0;
@@ -200,6 +219,19 @@ dsc_status dsc_lowrank_fwd(const void *x, const void *z, const void *U, void *y,
   return hip_status(dsc::lowrank_launch(a));
 }
 
+dsc_status dsc_lowrank_fwd(const void *x, const void *z, const void *U, void *y, int64_t B,
+                           int64_t T, int64_t D, int W, int H, int R, dsc_dtype dtype,
+                           unsigned flags, void *stream) {
+  return lowrank_fwd_common(x, z, U, nullptr, false, y, B, T, D, W, H, R, dtype, flags, stream);
+}
+
+dsc_status dsc_lowrank_fwd_varlen(const void *x, const void *z, const void *U,
+                                  const int32_t *pos, void *y, int64_t B, int64_t T, int64_t D,
+                                  int W, int H, int R, dsc_dtype dtype, unsigned flags,
+                                  void *stream) {
+  return lowrank_fwd_common(x, z, U, pos, true, y, B, T, D, W, H, R, dtype, flags, stream);
+}
+
 size_t dsc_lowrank_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int W, int H, int R,
                                        dsc_dtype dtype) {
   int V = 0;
@@ -207,29 +239,33 @@ size_t dsc_lowrank_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int W, i
   return dsc::lr_bwd_plan(B, T, D, W, H, R, dtype == DSC_BF16).bytes;
 }
 
-dsc_status dsc_lowrank_bwd(const void *x, const void *z, const void *U, const void *dy,
-                           void *dx, void *dz, void *dU, void *workspace,
-                           size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int W,
-                           int H, int R, dsc_dtype dtype, unsigned flags, void *stream) {
+static dsc_status lowrank_bwd_common(const void *x, const void *z, const void *U,
+                                     const int32_t *pos, bool varlen, const void *dy, void *dx,
+                                     void *dz, void *dU, void *workspace,
+                                     size_t workspace_bytes, int64_t B, int64_t T, int64_t D,
+                                     int W, int H, int R, dsc_dtype dtype, unsigned flags,
+                                     void *stream) {
   int V = 0;
   dsc_status st = lowrank_check(B, T, D, W, H, R, dtype, flags, &V);
   if (st != DSC_OK) return st;
   const int es = dtype == DSC_BF16 ? 2 : 4;
   const int64_t n_act = B * T * D, n_z = B * T * R, n_U = (int64_t)R * (D / H) * W;
   const dsc::LrBwdPlan p = dsc::lr_bwd_plan(B, T, D, W, H, R, dtype == DSC_BF16);
-  Span s[8] = {span("x", x, n_act, es, false),   span("z", z, n_z, es, false),
+  Span s[9] = {span("x", x, n_act, es, false),   span("z", z, n_z, es, false),
                span("U", U, n_U, es, false),     span("dy", dy, n_act, es, false),
                span("dx", dx, n_act, es, true),  span("dz", dz, n_z, es, true),
                span("dU", dU, n_U, es, true),
-               span("workspace", workspace, (int64_t)p.bytes, 1, true)};
+               span("workspace", workspace, (int64_t)p.bytes, 1, true),
+               span("pos", pos, varlen ? B * T : 0, 4, false)};
   if (p.bytes > 0 && workspace_bytes < p.bytes)
     return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed",
                 workspace_bytes, p.bytes);
   if (p.bytes > 0 && workspace == nullptr)
     return fail(DSC_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", p.bytes);
-  if ((st = check_ptrs(s, 8)) != DSC_OK) return st;
+  if ((st = check_ptrs(s, 9)) != DSC_OK) return st;
   dsc::LrArgs a{};
   a.x = x; a.z = z; a.U = U; a.dy = dy; a.dx = dx; a.dz = dz; a.dU = dU; a.ws = workspace;
+  a.pos = varlen ? pos : nullptr;
   a.B = B; a.T = T; a.D = D; a.W = W; a.H = H; a.R = R;
   a.bf16 = dtype == DSC_BF16;
   a.residual = (flags & DSC_RESIDUAL) != 0;
@@ -237,6 +273,23 @@ dsc_status dsc_lowrank_bwd(const void *x, const void *z, const void *U, const vo
   a.bwd = true;
   a.stream = stream;
   return hip_status(dsc::lowrank_launch(a));
+}
+
+dsc_status dsc_lowrank_bwd(const void *x, const void *z, const void *U, const void *dy,
+                           void *dx, void *dz, void *dU, void *workspace,
+                           size_t workspace_bytes, int64_t B, int64_t T, int64_t D, int W,
+                           int H, int R, dsc_dtype dtype, unsigned flags, void *stream) {
+  return lowrank_bwd_common(x, z, U, nullptr, false, dy, dx, dz, dU, workspace,
+                            workspace_bytes, B, T, D, W, H, R, dtype, flags, stream);
+}
+
+dsc_status dsc_lowrank_bwd_varlen(const void *x, const void *z, const void *U,
+                                  const int32_t *pos, const void *dy, void *dx, void *dz,
+                                  void *dU, void *workspace, size_t workspace_bytes, int64_t B,
+                                  int64_t T, int64_t D, int W, int H, int R, dsc_dtype dtype,
+                                  unsigned flags, void *stream) {
+  return lowrank_bwd_common(x, z, U, pos, true, dy, dx, dz, dU, workspace, workspace_bytes, B,
+                            T, D, W, H, R, dtype, flags, stream);
 }
 
 static dsc_status decode_common(const void *x, const void *w, const void *z, const void *U,

@@ -8,8 +8,11 @@
 
 namespace dsc {
 
+// pos: optional int32 (B, T) document positions of packed rows (tap k of
+// token t is used only when k <= pos[b,t]); nullptr for plain rows.
 struct HwArgs {
   const void *x, *w, *dy;
+  const int32_t *pos;
   void *y, *dx, *dw;
   int64_t B, T, D;
   int W, H;
@@ -19,6 +22,7 @@ struct HwArgs {
 
 struct LrArgs {
   const void *x, *z, *U, *dy;
+  const int32_t *pos;  // as in HwArgs
   void *y, *dx, *dz, *dU, *ws;
   int64_t B, T, D;
   int W, H, R;

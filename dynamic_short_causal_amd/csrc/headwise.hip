@@ -14,6 +14,11 @@
 // cache); when a group spans L > 1 lanes the filter gradient is summed across
 // those lanes with butterfly shuffles.  Every output element has one writer.
 //
+// Packed rows (VL): with document positions pos (B, T), the taps of token t
+// beyond pos[b,t] are zeroed before use, which removes every term that would
+// reach into the previous document, in the forward, in dx and in dw alike.
+// pos is uniform across a wave (one token at a time), so it is a scalar load.
+//
 // Cache policy: x, w, dy are read and y, dx written once per call, so they
 // are all loaded and stored non-temporally (measured on MI355X with inputs
 // that are not cache-resident: 3 % faster forward, 9 % faster backward).
@@ -35,10 +40,22 @@ template <typename E, int GPV> struct Geo {
 // ---------------------------------------------------------------------------
 // Forward: y[t] = act(sum_k w[t,g,k] x[t-k]) + rho x[t]
 // ---------------------------------------------------------------------------
-template <typename E, int W, int GPV, bool ACT>
+// zero the taps of a token beyond its document position p (packed rows); tap
+// 0 always stays, so a negative p acts as 0
+template <int W, int NG>
+__device__ __forceinline__ void mask_taps(float (&taps)[NG * W], int p) {
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+    for (int k = 1; k < W; ++k)
+      if (k > p) taps[gi * W + k] = 0.f;
+}
+
+template <typename E, int W, int GPV, bool ACT, bool VL>
 __global__ __launch_bounds__(kThreads) void hw_fwd_kernel(
-    const E *__restrict__ x, const E *__restrict__ w, E *__restrict__ y, int T,
-    int64_t D, int64_t G, int H, int nvec, int nvb, int TC, int nchunk, float rho) {
+    const E *__restrict__ x, const E *__restrict__ w, const int32_t *__restrict__ pos,
+    E *__restrict__ y, int T, int64_t D, int64_t G, int H, int nvec, int nvb, int TC,
+    int nchunk, float rho) {
   constexpr int V = Vw<E>::n;
   constexpr int UN = 4;  // tokens loaded ahead per step
   int bid = blockIdx.x;
@@ -93,6 +110,7 @@ __global__ __launch_bounds__(kThreads) void hw_fwd_kernel(
         unpack<E>(xr[u], win[0]);
         float taps[GPV * W];
         unpack_row<E, GPV * W>(wr[u], taps);
+        if constexpr (VL) mask_taps<W, GPV>(taps, pos[(int64_t)b * T + t + u]);
         float o[V];
 #pragma unroll
         for (int i = 0; i < V; ++i) {
@@ -116,12 +134,12 @@ __global__ __launch_bounds__(kThreads) void hw_fwd_kernel(
 // t-1-j; token t adds w[t,g,k] ds[t] to token t-k, after which token t-W+1 is
 // complete and is stored.  Tokens t1 .. t1+W-2 (the right halo) only feed dx.
 // ---------------------------------------------------------------------------
-template <typename E, int W, int GPV, bool ACT>
+template <typename E, int W, int GPV, bool ACT, bool VL>
 __device__ __forceinline__ void hw_bwd_token(
     const E *xp, const E *dyp, const E *wp, E *dxp, E *dwp, int64_t D,
     int64_t wstride, int t, int t0, int t1, int T, int L, int lane_in_group,
     float rho, float (&win)[W][Geo<E, GPV>::V], float (&acc)[W > 1 ? W - 1 : 1][Geo<E, GPV>::V],
-    uint4 xr, uint4 dyr, const RowBits<E, GPV * W> &wr) {
+    uint4 xr, uint4 dyr, const RowBits<E, GPV * W> &wr, int p) {
   constexpr int V = Vw<E>::n;
   constexpr int HS = Geo<E, GPV>::HS;
   const bool in_chunk = t < t1;
@@ -134,6 +152,7 @@ __device__ __forceinline__ void hw_bwd_token(
   if (in_seq) {
     unpack<E>(dyr, dyv);
     unpack_row<E, GPV * W>(wr, taps);
+    if constexpr (VL) mask_taps<W, GPV>(taps, p);
     if (ACT || in_chunk) {
       unpack<E>(xr, win[0]);
     } else {
@@ -160,7 +179,7 @@ __device__ __forceinline__ void hw_bwd_token(
   }
   // filter gradient of token t (inside the chunk only)
   if (in_chunk) {
-    float p[GPV][W];
+    float pw[GPV][W];
 #pragma unroll
     for (int gi = 0; gi < GPV; ++gi)
 #pragma unroll
@@ -168,20 +187,20 @@ __device__ __forceinline__ void hw_bwd_token(
         float a = 0.f;
 #pragma unroll
         for (int h = 0; h < HS; ++h) a = fmaf(ds[gi * HS + h], win[k][gi * HS + h], a);
-        p[gi][k] = a;
+        pw[gi][k] = (VL && k > 0 && k > p) ? 0.f : a;
       }
     if constexpr (GPV == 1) {
       // sum over the L lanes of the group (aligned, contiguous lanes)
       for (int m = 1; m < L; m <<= 1)
 #pragma unroll
-        for (int k = 0; k < W; ++k) p[0][k] += __shfl_xor(p[0][k], m);
+        for (int k = 0; k < W; ++k) pw[0][k] += __shfl_xor(pw[0][k], m);
     }
     if (GPV > 1 || lane_in_group == 0) {
       float flat[GPV * W];
 #pragma unroll
       for (int gi = 0; gi < GPV; ++gi)
 #pragma unroll
-        for (int k = 0; k < W; ++k) flat[gi * W + k] = p[gi][k];
+        for (int k = 0; k < W; ++k) flat[gi * W + k] = pw[gi][k];
       st_row<E, GPV * W>(dwp + (int64_t)t * wstride, flat);
     }
   }
@@ -206,11 +225,11 @@ __device__ __forceinline__ void hw_bwd_token(
   if (tau >= t0 && tau < t1) st16nt(dxp + (int64_t)tau * D, pack<E>(o));
 }
 
-template <typename E, int W, int GPV, bool ACT>
+template <typename E, int W, int GPV, bool ACT, bool VL>
 __global__ __launch_bounds__(kThreads) void hw_bwd_kernel(
     const E *__restrict__ x, const E *__restrict__ w, const E *__restrict__ dy,
-    E *__restrict__ dx, E *__restrict__ dw, int T, int64_t D, int64_t G, int H, int nvec,
-    int nvb, int TC, int nchunk, float rho) {
+    const int32_t *__restrict__ pos, E *__restrict__ dx, E *__restrict__ dw, int T, int64_t D,
+    int64_t G, int H, int nvec, int nvb, int TC, int nchunk, float rho) {
   constexpr int V = Vw<E>::n;
   constexpr int UN = 4;
   int bid = blockIdx.x;
@@ -270,8 +289,9 @@ __global__ __launch_bounds__(kThreads) void hw_bwd_kernel(
 #pragma unroll
     for (int u = 0; u < UN; ++u)
       if (t + u < t1)
-        hw_bwd_token<E, W, GPV, ACT>(xp, dyp, wp, dxp, dwp, D, wstride, t + u, t0, t1, T, L,
-                                     lane_in_group, rho, win, acc, xr[u], dyr[u], wr[u]);
+        hw_bwd_token<E, W, GPV, ACT, VL>(xp, dyp, wp, dxp, dwp, D, wstride, t + u, t0, t1, T, L,
+                                         lane_in_group, rho, win, acc, xr[u], dyr[u], wr[u],
+                                         VL ? pos[(int64_t)b * T + t + u] : 0);
   }
   // right halo: tokens t1 .. t1+W-2 complete dx of the chunk's last W-1 tokens
 #pragma unroll
@@ -279,13 +299,15 @@ __global__ __launch_bounds__(kThreads) void hw_bwd_kernel(
     const int t = t1 + j;
     uint4 xr = make_uint4(0, 0, 0, 0), dyr = make_uint4(0, 0, 0, 0);
     RowBits<E, GPV * W> wr = {};
+    int p = 0;
     if (t < T) {
       if (ACT) xr = ld16nt(xp + (int64_t)t * D);
       dyr = ld16nt(dyp + (int64_t)t * D);
       wr = ld_row<E, GPV * W, true>(wp + (int64_t)t * wstride);
+      if constexpr (VL) p = pos[(int64_t)b * T + t];
     }
-    hw_bwd_token<E, W, GPV, ACT>(xp, dyp, wp, dxp, dwp, D, wstride, t, t0, t1, T, L,
-                                 lane_in_group, rho, win, acc, xr, dyr, wr);
+    hw_bwd_token<E, W, GPV, ACT, VL>(xp, dyp, wp, dxp, dwp, D, wstride, t, t0, t1, T, L,
+                                     lane_in_group, rho, win, acc, xr, dyr, wr, p);
   }
 }
 
@@ -299,7 +321,7 @@ static int pick_chunk(int T) {
   return T;
 }
 
-template <typename E, int W, int GPV, bool ACT>
+template <typename E, int W, int GPV, bool ACT, bool VL>
 static hipError_t launch_hw(const HwArgs &a) {
   constexpr int V = Vw<E>::n;
   const int nvec = (int)(a.D / V);
@@ -311,20 +333,26 @@ static hipError_t launch_hw(const HwArgs &a) {
   const float rho = a.residual ? 1.f : 0.f;
   hipStream_t s = (hipStream_t)a.stream;
   if (!a.bwd) {
-    hipLaunchKernelGGL((hw_fwd_kernel<E, W, GPV, ACT>), dim3((unsigned)nblocks), dim3(kThreads),
-                       0, s, (const E *)a.x, (const E *)a.w, (E *)a.y, (int)a.T, a.D, G, a.H,
-                       nvec, nvb, TC, nchunk, rho);
+    hipLaunchKernelGGL((hw_fwd_kernel<E, W, GPV, ACT, VL>), dim3((unsigned)nblocks),
+                       dim3(kThreads), 0, s, (const E *)a.x, (const E *)a.w, a.pos, (E *)a.y,
+                       (int)a.T, a.D, G, a.H, nvec, nvb, TC, nchunk, rho);
   } else {
-    hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPV, ACT>), dim3((unsigned)nblocks), dim3(kThreads),
-                       0, s, (const E *)a.x, (const E *)a.w, (const E *)a.dy, (E *)a.dx,
-                       (E *)a.dw, (int)a.T, a.D, G, a.H, nvec, nvb, TC, nchunk, rho);
+    hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPV, ACT, VL>), dim3((unsigned)nblocks),
+                       dim3(kThreads), 0, s, (const E *)a.x, (const E *)a.w, (const E *)a.dy,
+                       a.pos, (E *)a.dx, (E *)a.dw, (int)a.T, a.D, G, a.H, nvec, nvb, TC,
+                       nchunk, rho);
   }
   return hipGetLastError();
 }
 
+template <typename E, int W, int GPV, bool ACT>
+static hipError_t dispatch_vl(const HwArgs &a) {
+  return a.pos ? launch_hw<E, W, GPV, ACT, true>(a) : launch_hw<E, W, GPV, ACT, false>(a);
+}
+
 template <typename E, int W, int GPV>
 static hipError_t dispatch_act(const HwArgs &a) {
-  return a.act ? launch_hw<E, W, GPV, true>(a) : launch_hw<E, W, GPV, false>(a);
+  return a.act ? dispatch_vl<E, W, GPV, true>(a) : dispatch_vl<E, W, GPV, false>(a);
 }
 
 template <typename E, int W>

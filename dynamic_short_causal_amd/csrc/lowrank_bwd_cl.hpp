@@ -109,23 +109,32 @@ template <int W> struct LrBwdClGeo {
   static constexpr int o_ds = o_z + 32 * ZP;
   static constexpr int o_chk = o_ds + kClCB * DSP;
   static constexpr int o_dz = o_chk + kClWaves * CHK;
-  static constexpr int bytes = o_dz + kClWaves * 64 * 16;
+  static constexpr int o_pos = o_dz + kClWaves * 64 * 16;  // 32 document positions (VL)
+  static constexpr int bytes = o_pos + 32 * 4;
 };
 
 // Waves per SIMD: as many as the compiler fits without spilling (read off the
 // kernel resource-usage report; the register count grows with W).
-template <int W, bool ACT>
+template <int W, bool ACT, bool VL>
 constexpr int lr_bwd_cl_min_waves() {
-  if constexpr (ACT) return W <= 7 ? 2 : 1;
-  else return W <= 4 ? 3 : 2;
+  if constexpr (VL) {  // the position masks take a few more registers
+    if constexpr (ACT) return W <= 6 ? 2 : 1;
+    else return W <= 3 ? 3 : W <= 7 ? 2 : 1;
+  } else {
+    if constexpr (ACT) return W <= 7 ? 2 : 1;
+    else return W <= 4 ? 3 : 2;
+  }
 }
 
-template <int W, bool ACT>
-__global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void lr_bwd_cl_kernel(
+// Packed rows (VL): a 32-entry ring of document positions; taps k >= 1 of a
+// token beyond its position are zeroed in the dx filters (tokens t+k), in the
+// SiLU recomputation and in dw (own tokens), hence also in dz and dU.
+template <int W, bool ACT, bool VL>
+__global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) void lr_bwd_cl_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ z, const bf16 *__restrict__ U,
-    const bf16 *__restrict__ dy, bf16 *__restrict__ dx, float *__restrict__ dzp,
-    float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk, int ncb,
-    int64_t N, float rho) {
+    const bf16 *__restrict__ dy, const int32_t *__restrict__ pos, bf16 *__restrict__ dx,
+    float *__restrict__ dzp, float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk,
+    int ncb, int64_t N, float rho) {
   using Gc = LrBwdClGeo<W>;
   constexpr int XP = Gc::XP, ZP = Gc::ZP, DSP = Gc::DSP, NHQ = Gc::NHQ, NDQ = Gc::NDQ, NG = kClNG;
   constexpr int RP = 16;
@@ -133,6 +142,7 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
   unsigned char *xring = smem + Gc::o_x, *dyslab = smem + Gc::o_dy, *dxst = smem + Gc::o_dx,
                 *zring = smem + Gc::o_z, *dsring = smem + Gc::o_ds;
   float *dzbuf = reinterpret_cast<float *>(smem + Gc::o_dz);
+  int *pring = reinterpret_cast<int *>(smem + Gc::o_pos);
 
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, n = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -212,9 +222,14 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
 
   uint4 xn, dyn;
   bf16 zn;
+  int pn = 0;
   auto issue = [&](int st) {
     const int t = t0 + 16 * st;
     const bool halo = st == tiles;
+    if constexpr (VL) {
+      const brsrc rp = mk_rsrc(pos + seq + t, (int64_t)(min(T, t + 16) - t) * 4);
+      pn = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, tid < 16 ? (uint32_t)tid * 4 : kOOB, 0, 0);
+    }
     const brsrc rz = slab(z, t, T, R, R);
     const brsrc rd = slab(dy, t, T, D, D);
     const brsrc rx = slab(x, t, T, D, D);
@@ -228,6 +243,7 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
     if (ACT || !halo) *reinterpret_cast<uint4 *>(xring + ((t + cr) & 31) * XP + cv * 16) = xn;
     *reinterpret_cast<uint4 *>(dyslab + cr * XP + cv * 16) = dyn;
     if (z_on) reinterpret_cast<bf16 *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn;
+    if (VL && tid < 16) pring[(t + tid) & 31] = pn;
   };
 
   float dyp[NG][4] = {};
@@ -254,6 +270,12 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
         for (int e = 0; e < 4; ++e) xw[u][4 * h + e] = bf2f(xv[e]);
       }
     }
+    // document positions of the lane's own tokens t+4q+e (VL)
+    int pown[4] = {W, W, W, W};
+    if constexpr (VL) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pown[e] = pring[(t + 4 * q + e) & 31];
+    }
     if constexpr (ACT) {
       const s16x4 az = *reinterpret_cast<const s16x4 *>(zring + ((t + n) & 31) * ZP + 8 * q);
 #pragma unroll
@@ -263,7 +285,8 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
         for (int k = 0; k < W; ++k) {
           const f32x4 wk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(az, bu[u][k], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sa[e] = fmaf(wk[e], xw[u][X0 + e - k], sa[e]);
+          for (int e = 0; e < 4; ++e)
+            sa[e] = fmaf((VL && k > 0 && k > pown[e]) ? 0.f : wk[e], xw[u][X0 + e - k], sa[e]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) ds[u][e] = dyc[u][e] * silu_grad_f(sa[e]);
@@ -280,6 +303,10 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
           f32x4{ds[u][0], ds[u][1], ds[u][2], ds[u][3]};
     __builtin_amdgcn_wave_barrier();
     if (st > 0) {
+      // document positions of tokens t-16+4q+i, i < W+3 (VL)
+      int psh[W + 3];
+#pragma unroll
+      for (int i = 0; i < W + 3; ++i) psh[i] = VL ? pring[(t - 16 + 4 * q + i) & 31] : W;
       s16x4 az[W];
 #pragma unroll
       for (int k = 0; k < W; ++k)
@@ -301,7 +328,8 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
           const float ini = k == 0 ? rho_tap : 0.f;
           const f32x4 wk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(az[k], bu[u][k], f32x4{ini, ini, ini, ini}, 0, 0, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = fmaf(wk[e], dw[e + k], o[e]);
+          for (int e = 0; e < 4; ++e)
+            o[e] = fmaf((VL && k > 0 && k > psh[e + k]) ? 0.f : wk[e], dw[e + k], o[e]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -322,8 +350,12 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT>())) void l
         s16x4 bdw[W];
 #pragma unroll
         for (int k = 0; k < W; ++k) {
-          const uint32_t p0 = pack_bf16x2(ds[u][0] * xw[u][X0 - k], ds[u][1] * xw[u][X0 + 1 - k]);
-          const uint32_t p1 = pack_bf16x2(ds[u][2] * xw[u][X0 + 2 - k], ds[u][3] * xw[u][X0 + 3 - k]);
+          float pr[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pr[e] = (VL && k > 0 && k > pown[e]) ? 0.f : ds[u][e] * xw[u][X0 + e - k];
+          const uint32_t p0 = pack_bf16x2(pr[0], pr[1]);
+          const uint32_t p1 = pack_bf16x2(pr[2], pr[3]);
           bdw[k] = __builtin_bit_cast(s16x4, make_uint2(p0, p1));
           accU[u][k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(azt, bdw[k], accU[u][k], 0, 0, 0);
         }

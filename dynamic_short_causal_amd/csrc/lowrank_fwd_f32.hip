@@ -1,6 +1,6 @@
-// lowrank_fwd_f32.hip -- instantiates the low-rank fwd launchers for f32.
+// lowrank_fwd_f32.hip -- instantiates the low-rank fwd launchers for f32 (plain rows).
 #include "lowrank_launch.hpp"
 
 namespace dsc {
-template hipError_t lr_dispatch<float, false>(const LrArgs &a);
+template hipError_t lr_dispatch<float, false, false>(const LrArgs &a);
 }  // namespace dsc

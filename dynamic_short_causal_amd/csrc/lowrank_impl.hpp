@@ -211,10 +211,13 @@ template <typename E, int W, int GPV> struct LrFwdGeo {
   static constexpr int bytes = 32 * XR + 16 * SP;
 };
 
-template <typename E, int W, int GPV, bool ACT>
+// Packed rows (VL): taps k >= 1 of a token beyond its document position are
+// zeroed right after the filters are formed, before any use.
+template <typename E, int W, int GPV, bool ACT, bool VL>
 __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
-    const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U, E *__restrict__ y,
-    int T, int D, int R, int TC, int nchunk, int ncb, float rho) {
+    const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U,
+    const int32_t *__restrict__ pos, E *__restrict__ y, int T, int D, int R, int TC,
+    int nchunk, int ncb, float rho) {
   using Gm = LrGeo<E, W, GPV>;
   using Fg = LrFwdGeo<E, W, GPV>;
   constexpr int V = Gm::V, NU = Gm::NU, NP = Gm::NP, KS = Gm::KS;
@@ -264,8 +267,10 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
   constexpr int PF = 4;
   typename WFrag<Gm::BF>::T zn[PF][KS];
   uint4 xn[PF][NPASS];
+  int pn[PF];  // document position of the lane's token (VL)
   auto issue = [&](int t, int sl) {  // sl: compile-time after unrolling
     load_zB<E, KS>(z, seq + t + j, t + j < t1, R, q, zn[sl]);
+    if constexpr (VL) pn[sl] = pos[seq + min(t + j, t1 - 1)];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
       const int tr = t + p * RPP + rr;
@@ -286,10 +291,18 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
     typename WFrag<Gm::BF>::T bz[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) bz[ks] = zn[sl][ks];
+    const int pj = VL ? pn[sl] : 0;
     if (t + 16 * PF < t1) issue(t + 16 * PF, sl);  // workgroup-uniform
     f32x4 wacc[W][NP];
 #pragma unroll
     for (int k = 0; k < W; ++k) gen_tap<E, W, GPV>(aw[k], bz, wacc[k]);
+    if constexpr (VL) {
+#pragma unroll
+      for (int k = 1; k < W; ++k)
+        if (k > pj)
+#pragma unroll
+          for (int p = 0; p < NP; ++p) wacc[k][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -384,7 +397,8 @@ template <typename E, int W, int GPV> struct LrBwdGeo {
   static constexpr int o_z = o_dx + 16 * SP;
   static constexpr int o_dz = o_z + 32 * ZP;
   static constexpr int o_dwt = o_dz + 4 * 64 * 16;
-  static constexpr int bytes = o_dwt + 4 * dwt_wave;
+  static constexpr int o_pos = o_dwt + 4 * dwt_wave;  // 32 document positions (VL)
+  static constexpr int bytes = o_pos + 32 * 4;
 };
 
 template <typename E, int W, int GPV>
@@ -411,12 +425,15 @@ constexpr int lr_bwd_min_waves() {
   else return GPV == 4 && W >= 7 ? 2 : 3;
 }
 
-template <typename E, int W, int GPV>
+// Packed rows (VL): a 32-entry ring of document positions beside the z ring;
+// a tap k >= 1 of token t is zeroed where k > pos[t], in the filters of dx and
+// of the SiLU recomputation and in dw (hence in dz and dU).
+template <typename E, int W, int GPV, bool VL>
 __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void lr_bwd_kernel(
     const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U,
-    const E *__restrict__ dy, E *__restrict__ dx, float *__restrict__ dzp,
-    float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk, int ncb, int64_t N,
-    float rho, int act) {
+    const E *__restrict__ dy, const int32_t *__restrict__ pos, E *__restrict__ dx,
+    float *__restrict__ dzp, float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk,
+    int ncb, int64_t N, float rho, int act) {
   using Gm = LrGeo<E, W, GPV>;
   using Bg = LrBwdGeo<E, W, GPV>;
   constexpr bool BF = Gm::BF;
@@ -432,6 +449,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
   unsigned char *xring = smem + Bg::o_x, *dring = smem + Bg::o_ds, *dxstage = smem + Bg::o_dx,
                 *zring = smem + Bg::o_z;
   float *dzbuf = reinterpret_cast<float *>(smem + Bg::o_dz);
+  int *pring = reinterpret_cast<int *>(smem + Bg::o_pos);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, j = lane & 15;
   int bid = blockIdx.x;
@@ -536,9 +554,14 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
 
   uint4 xn[PF][NPASS], dyn[PF][NPASS];
   E zn[PF];
+  int pn[PF];
   auto issue = [&](int st, int sl) {
     const int t = t0 + 16 * st;
     const bool halo = st == tiles;
+    if constexpr (VL) {
+      const brsrc rp = mk_rsrc(pos + seq + t, (int64_t)(min(T, t + 16) - t) * 4);
+      pn[sl] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, tid < 16 ? (uint32_t)tid * 4 : kOOB, 0, 0);
+    }
     const brsrc rdy = slab(dy, t, T);
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
@@ -573,6 +596,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
       }
     }
     if (z_on) reinterpret_cast<E *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn[sl];
+    if (VL && tid < 16) pring[(t + tid) & 31] = pn[sl];
   };
 
   float dyp[NU][V];  // (SiLU only) dy of the previous tile, for the residual term of its dx
@@ -610,6 +634,14 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
       f32x4 wacc[W][NP];
 #pragma unroll
       for (int k = 0; k < W; ++k) gen_tap<E, W, GPV>(aw[k], bz, wacc[k]);
+      if constexpr (VL) {
+        const int pj = pring[tau & 31];
+#pragma unroll
+        for (int k = 1; k < W; ++k)
+          if (k > pj)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) wacc[k][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         float sacc[V];
@@ -646,6 +678,9 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
         zfrag(tp + k, bzs);
         f32x4 wk[NP];
         gen_tap_init<E, W, GPV>(aw[k], bzs, wk, k == 0 ? rho_tap : 0.f);
+        if (VL && k > 0 && k > pring[(tp + k) & 31])
+#pragma unroll
+          for (int p = 0; p < NP; ++p) wk[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
           const f32x4 *src = dslot(tp + k, u);
@@ -668,6 +703,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
       // filter-gradient slots; a chunk ends inside a tile only at the sequence
       // end, where ds is zero, so no lane needs masking
       float dwv[NS];
+      const int pown = VL ? pring[tau & 31] : W;
 #pragma unroll
       for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -684,7 +720,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void l
             float a = 0.f;
 #pragma unroll
             for (int h = 0; h < Gm::H; ++h) a = fmaf(ds[u][gi * Gm::H + h], xk[gi * Gm::H + h], a);
-            dwv[k * NG + u * GPV + gi] = a;
+            dwv[k * NG + u * GPV + gi] = (VL && k > 0 && k > pown) ? 0.f : a;
           }
         }
       constexpr int NPAIR = (NS + 1) / 2;

@@ -8,7 +8,7 @@
 
 namespace dsc {
 
-template <typename E, int W, int GPV, bool ACT>
+template <typename E, int W, int GPV, bool ACT, bool VL>
 static hipError_t launch_lr_fwd(const LrArgs &a) {
   using Gm = LrGeo<E, W, GPV>;
   hipStream_t s = (hipStream_t)a.stream;
@@ -19,9 +19,10 @@ static hipError_t launch_lr_fwd(const LrArgs &a) {
   const int64_t nblocks = a.B * nchunk * (int64_t)ncb;
   if (nblocks == 0) return hipSuccess;
   constexpr int smem = LrFwdGeo<E, W, GPV>::bytes;
-  hipLaunchKernelGGL((lr_fwd_kernel<E, W, GPV, ACT>), dim3((unsigned)nblocks),
+  hipLaunchKernelGGL((lr_fwd_kernel<E, W, GPV, ACT, VL>), dim3((unsigned)nblocks),
                      dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
-                     (const E *)a.U, (E *)a.y, (int)a.T, (int)a.D, a.R, TC, nchunk, ncb, rho);
+                     (const E *)a.U, a.pos, (E *)a.y, (int)a.T, (int)a.D, a.R, TC, nchunk, ncb,
+                     rho);
   return hipGetLastError();
 }
 
@@ -30,7 +31,7 @@ static hipError_t launch_lr_reduce(const LrArgs &a, const LrBwdPlan &p, const fl
                                    const float *dUp);
 
 // per-channel filters in bf16: one channel per lane (lowrank_bwd_cl.hpp)
-template <int W>
+template <int W, bool VL>
 static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
   hipStream_t s = (hipStream_t)a.stream;
   const float rho = a.residual ? 1.f : 0.f;
@@ -43,25 +44,25 @@ static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
     constexpr int smem = LrBwdClGeo<W>::bytes;
     const int64_t N = a.B * a.T;
     if (a.act)
-      hipLaunchKernelGGL((lr_bwd_cl_kernel<W, true>), dim3((unsigned)nblocks), dim3(kClThreads),
-                         smem, s, (const bf16 *)a.x, (const bf16 *)a.z, (const bf16 *)a.U,
-                         (const bf16 *)a.dy, (bf16 *)a.dx, dzp, dUp, (int)a.T, (int)a.D,
-                         a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
+      hipLaunchKernelGGL((lr_bwd_cl_kernel<W, true, VL>), dim3((unsigned)nblocks),
+                         dim3(kClThreads), smem, s, (const bf16 *)a.x, (const bf16 *)a.z,
+                         (const bf16 *)a.U, (const bf16 *)a.dy, a.pos, (bf16 *)a.dx, dzp, dUp,
+                         (int)a.T, (int)a.D, a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
     else
-      hipLaunchKernelGGL((lr_bwd_cl_kernel<W, false>), dim3((unsigned)nblocks), dim3(kClThreads),
-                         smem, s, (const bf16 *)a.x, (const bf16 *)a.z, (const bf16 *)a.U,
-                         (const bf16 *)a.dy, (bf16 *)a.dx, dzp, dUp, (int)a.T, (int)a.D,
-                         a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
+      hipLaunchKernelGGL((lr_bwd_cl_kernel<W, false, VL>), dim3((unsigned)nblocks),
+                         dim3(kClThreads), smem, s, (const bf16 *)a.x, (const bf16 *)a.z,
+                         (const bf16 *)a.U, (const bf16 *)a.dy, a.pos, (bf16 *)a.dx, dzp, dUp,
+                         (int)a.T, (int)a.D, a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return launch_lr_reduce<bf16>(a, p, dzp, dUp);
 }
 
-template <typename E, int W, int GPV>
+template <typename E, int W, int GPV, bool VL>
 static hipError_t launch_lr_bwd(const LrArgs &a) {
   if constexpr (sizeof(E) == 2 && GPV == 8) {  // H == 1
-    return launch_lr_bwd_cl<W>(a);
+    return launch_lr_bwd_cl<W, VL>(a);
   } else {
     hipStream_t s = (hipStream_t)a.stream;
     const float rho = a.residual ? 1.f : 0.f;
@@ -72,10 +73,11 @@ static hipError_t launch_lr_bwd(const LrArgs &a) {
     const int64_t nblocks = a.B * p.nchunk * p.ncb;
     if (nblocks > 0) {
       constexpr int smem = LrBwdGeo<E, W, GPV>::bytes;
-      hipLaunchKernelGGL((lr_bwd_kernel<E, W, GPV>), dim3((unsigned)nblocks),
+      hipLaunchKernelGGL((lr_bwd_kernel<E, W, GPV, VL>), dim3((unsigned)nblocks),
                          dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
-                         (const E *)a.U, (const E *)a.dy, (E *)a.dx, dzp, dUp, (int)a.T,
-                         (int)a.D, a.R, p.tc, (int)p.nchunk, (int)p.ncb, N, rho, a.act ? 1 : 0);
+                         (const E *)a.U, (const E *)a.dy, a.pos, (E *)a.dx, dzp, dUp,
+                         (int)a.T, (int)a.D, a.R, p.tc, (int)p.nchunk, (int)p.ncb, N, rho,
+                         a.act ? 1 : 0);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -101,39 +103,41 @@ static hipError_t launch_lr_reduce(const LrArgs &a, const LrBwdPlan &p, const fl
 }
 
 // one 16-row rank block: the argument checks admit R <= 16 only
-template <typename E, int W, int GPV, bool BWD>
+template <typename E, int W, int GPV, bool BWD, bool VL>
 static hipError_t lr_rb(const LrArgs &a) {
   if constexpr (BWD) {
-    return launch_lr_bwd<E, W, GPV>(a);
+    return launch_lr_bwd<E, W, GPV, VL>(a);
   } else {
-    return a.act ? launch_lr_fwd<E, W, GPV, true>(a) : launch_lr_fwd<E, W, GPV, false>(a);
+    return a.act ? launch_lr_fwd<E, W, GPV, true, VL>(a) : launch_lr_fwd<E, W, GPV, false, VL>(a);
   }
 }
 
-template <typename E, int W, bool BWD>
+template <typename E, int W, bool BWD, bool VL>
 static hipError_t lr_gpv(const LrArgs &a) {
   constexpr int V = Vw<E>::n;
   switch (V / a.H) {
-    case 1: return lr_rb<E, W, 1, BWD>(a);
-    case 2: return lr_rb<E, W, 2, BWD>(a);
-    case 4: return lr_rb<E, W, 4, BWD>(a);
+    case 1: return lr_rb<E, W, 1, BWD, VL>(a);
+    case 2: return lr_rb<E, W, 2, BWD, VL>(a);
+    case 4: return lr_rb<E, W, 4, BWD, VL>(a);
     default:
-      if constexpr (V == 8) return lr_rb<E, W, 8, BWD>(a);
+      if constexpr (V == 8) return lr_rb<E, W, 8, BWD, VL>(a);
       return hipErrorInvalidValue;
   }
 }
 
-template <typename E, bool BWD>
+// VL: rows packed with documents (a.pos set); instantiated in their own
+// translation units so the two builds compile in parallel
+template <typename E, bool BWD, bool VL>
 hipError_t lr_dispatch(const LrArgs &a) {
   switch (a.W) {
-    case 1: return lr_gpv<E, 1, BWD>(a);
-    case 2: return lr_gpv<E, 2, BWD>(a);
-    case 3: return lr_gpv<E, 3, BWD>(a);
-    case 4: return lr_gpv<E, 4, BWD>(a);
-    case 5: return lr_gpv<E, 5, BWD>(a);
-    case 6: return lr_gpv<E, 6, BWD>(a);
-    case 7: return lr_gpv<E, 7, BWD>(a);
-    case 8: return lr_gpv<E, 8, BWD>(a);
+    case 1: return lr_gpv<E, 1, BWD, VL>(a);
+    case 2: return lr_gpv<E, 2, BWD, VL>(a);
+    case 3: return lr_gpv<E, 3, BWD, VL>(a);
+    case 4: return lr_gpv<E, 4, BWD, VL>(a);
+    case 5: return lr_gpv<E, 5, BWD, VL>(a);
+    case 6: return lr_gpv<E, 6, BWD, VL>(a);
+    case 7: return lr_gpv<E, 7, BWD, VL>(a);
+    case 8: return lr_gpv<E, 8, BWD, VL>(a);
     default: return hipErrorInvalidValue;
   }
 }

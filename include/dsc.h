@@ -202,6 +202,38 @@ dsc_status dsc_static_bwd(const void *x, const void *w, const void *dy, void *dx
                           int64_t D, int W, int H, dsc_dtype dtype, unsigned flags,
                           void *stream);
 
+/*
+ * Rows packed with several documents.  pos (B, T), int32 in device memory,
+ * 16-byte aligned, holds each token's index inside its document (0 at a
+ * document start; entries must be >= 0).  Tap k >= 1 of token t is used only
+ * when k <= pos[b,t], so no tap reaches into the previous document; every
+ * other argument, layout and error is that of the call without _varlen, and
+ * with pos[b,t] = t the results equal it.  The masked taps contribute nothing
+ * to y and dx, and their dw (head-wise) or their share of dz and dU
+ * (low-rank) is zero.  The pages train on whole rows and do not discuss
+ * packing; this is a training-side layout.
+ */
+dsc_status dsc_headwise_fwd_varlen(const void *x, const void *w, const int32_t *pos, void *y,
+                                   int64_t B, int64_t T, int64_t D, int W, int H,
+                                   dsc_dtype dtype, unsigned flags, void *stream);
+
+dsc_status dsc_headwise_bwd_varlen(const void *x, const void *w, const int32_t *pos,
+                                   const void *dy, void *dx, void *dw, int64_t B, int64_t T,
+                                   int64_t D, int W, int H, dsc_dtype dtype, unsigned flags,
+                                   void *stream);
+
+dsc_status dsc_lowrank_fwd_varlen(const void *x, const void *z, const void *U,
+                                  const int32_t *pos, void *y, int64_t B, int64_t T, int64_t D,
+                                  int W, int H, int R, dsc_dtype dtype, unsigned flags,
+                                  void *stream);
+
+/* Workspace as for dsc_lowrank_bwd (dsc_lowrank_bwd_workspace_bytes). */
+dsc_status dsc_lowrank_bwd_varlen(const void *x, const void *z, const void *U,
+                                  const int32_t *pos, const void *dy, void *dx, void *dz,
+                                  void *dU, void *workspace, size_t workspace_bytes, int64_t B,
+                                  int64_t T, int64_t D, int W, int H, int R, dsc_dtype dtype,
+                                  unsigned flags, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -226,3 +226,22 @@ def test_static_checks(lib):
     assert sbw(lib, ws=A + 3 * BIG + 16) == INVALID          # workspace overlaps dx
     assert sbw(lib, dw=A + BIG) == INVALID                   # dw overlaps w
     assert sbw(lib, fl=16) == UNSUP
+
+
+def test_varlen_checks(lib):
+    p = ctypes.c_void_p
+    POS = A + 9 * BIG
+    hv = lambda pos=POS, **kw: lib.dsc_headwise_fwd_varlen(
+        p(A), p(A + BIG), p(pos), p(A + 2 * BIG), kw.get("B", 1), 8, 64, 4, kw.get("H", 1), 1, 0,
+        None)
+    assert hv(pos=0) == INVALID                              # pos is NULL
+    assert hv(pos=POS + 4) == INVALID                        # not 16-byte aligned
+    assert hv(pos=A + 2 * BIG + 16) == INVALID               # y overlaps pos
+    assert hv(H=3) == INVALID                                # 64 % 3
+    assert hv(B=0, pos=0) == 0                               # empty: pos unused
+    lv = lambda pos=POS: lib.dsc_lowrank_bwd_varlen(
+        p(A), p(A + BIG), p(A + 2 * BIG), p(pos), p(A + 3 * BIG), p(A + 4 * BIG), p(A + 5 * BIG),
+        p(A + 6 * BIG), p(A + 7 * BIG), lib.dsc_lowrank_bwd_workspace_bytes(1, 8, 64, 4, 1, 16, 1),
+        1, 8, 64, 4, 1, 16, 1, 0, None)
+    assert lv(pos=0) == INVALID
+    assert lv(pos=A + 4 * BIG + 64) == INVALID               # dx overlaps pos
