@@ -248,6 +248,64 @@ def static_bench(dsc, di, torch, dev, steps, per_kernel_ms):
     return out
 
 
+def varlen_bench(dsc, di, torch, dev, steps, per_kernel_ms):
+    """The step's four ops on packed rows: every row of the batch holds
+    documents of 1..512 tokens (mean about 256), positions in pos (B, T).
+    Each op reads its own input copies; mean of `steps` event-timed launches.
+    Reported beside the plain ops' times (the masking overhead).  Not part of
+    the step."""
+    import numpy as np
+    B, T, D, W = WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"]
+    Hh, R, Hl = WORKLOAD["H_headwise"], WORKLOAD["R"], WORKLOAD["H_lowrank"]
+    rng = np.random.default_rng(98)
+    pos = np.zeros((B, T), dtype=np.int32)
+    for b in range(B):
+        t = 0
+        while t < T:
+            n = int(rng.integers(1, 513))
+            pos[b, t:t + n] = np.arange(min(n, T - t))
+            t += n
+    pd = torch.from_numpy(pos).to(dev)
+    stream = torch.cuda.current_stream()
+    mk = lambda shape, std, seed: di.randn(shape, std, seed, "bf16").to(dev)
+    G = D // Hh
+    xa, wa = mk((B, T, D), 1.0, 80), mk((B, T, G, W), 0.5, 81)
+    xb, wb, dyb = mk((B, T, D), 1.0, 82), mk((B, T, G, W), 0.5, 83), mk((B, T, D), 1.0, 84)
+    xc, zc = mk((B, T, D), 1.0, 85), mk((B, T, R), 1.0, 86)
+    Uc = mk((R, (D // Hl) * W), (1.0 / (R * W)) ** 0.5, 87)
+    xd, zd, dyd = mk((B, T, D), 1.0, 88), mk((B, T, R), 1.0, 89), mk((B, T, D), 1.0, 90)
+    y1, dx1, dw1 = torch.empty_like(xa), torch.empty_like(xa), torch.empty_like(wa)
+    y2, dx2, dz2, dU2 = (torch.empty_like(xa), torch.empty_like(xa), torch.empty_like(zc),
+                         torch.empty_like(Uc))
+    ws = dsc.lowrank_workspace(xd, zd, W, Hl)
+    ops = {
+        "headwise_fwd": lambda: dsc.dsc_headwise_fwd_varlen(xa, wa, pd, y1, Hh, True, False,
+                                                            stream),
+        "headwise_bwd": lambda: dsc.dsc_headwise_bwd_varlen(xb, wb, pd, dyb, dx1, dw1, Hh, True,
+                                                            False, stream),
+        "lowrank_fwd": lambda: dsc.dsc_lowrank_fwd_varlen(xc, zc, Uc, pd, y2, W, Hl, True, False,
+                                                          stream),
+        "lowrank_bwd": lambda: dsc.dsc_lowrank_bwd_varlen(xd, zd, Uc, pd, dyd, dx2, dz2, dU2, ws,
+                                                          W, Hl, True, False, stream),
+    }
+    out = {"documents": int((pos == 0).sum())}
+    for name, fn in ops.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+        out[name] = {"ms": round(ms, 4),
+                     "over_plain": round(ms / per_kernel_ms[name], 3)}
+    return out
+
+
 def decode_bench(dsc, di, torch, dev, iters=200):
     """One-token steps at serving batches, for head-wise H=16 and low-rank R=16
     H=1 at D=6144, W=4, bf16, residual.  Two timings of `iters` steps in a row:
@@ -419,6 +477,8 @@ def main():
     decode = decode_bench(dsc, di, torch, dev)
     print("bench: timing the static-filter comparator", file=sys.stderr, flush=True)
     static = static_bench(dsc, di, torch, dev, args.steps, per_kernel_ms)
+    print("bench: timing packed rows", file=sys.stderr, flush=True)
+    varlen = varlen_bench(dsc, di, torch, dev, args.steps, per_kernel_ms)
 
     nbytes = algorithmic_bytes(B, T, D, W, Hh, R, Hl)
     ms_per_step = elapsed / args.steps * 1e3
@@ -463,6 +523,7 @@ def main():
         "variants": variants,
         "decode": decode,
         "static_comparator": static,
+        "packed_rows": varlen,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -117,18 +117,16 @@ template <int W> struct LrBwdClGeo {
 // kernel resource-usage report; the register count grows with W).
 template <int W, bool ACT, bool VL>
 constexpr int lr_bwd_cl_min_waves() {
-  if constexpr (VL) {  // the position masks take a few more registers
-    if constexpr (ACT) return W <= 6 ? 2 : 1;
-    else return W <= 3 ? 3 : W <= 7 ? 2 : 1;
-  } else {
-    if constexpr (ACT) return W <= 7 ? 2 : 1;
-    else return W <= 4 ? 3 : 2;
-  }
+  // the position masks of packed rows tip the two widest cases over
+  if constexpr (VL && ((ACT && W == 7) || (!ACT && W == 8))) return 1;
+  if constexpr (ACT) return W <= 7 ? 2 : 1;
+  else return W <= 4 ? 3 : 2;
 }
 
-// Packed rows (VL): a 32-entry ring of document positions; taps k >= 1 of a
-// token beyond its position are zeroed in the dx filters (tokens t+k), in the
-// SiLU recomputation and in dw (own tokens), hence also in dz and dU.
+// Packed rows (VL): a 32-entry ring of document positions.  A tap k >= 1 of a
+// token beyond its position is dropped: for dx by zeroing that token's z row
+// in the tap-k A operand (one row per lane), for the SiLU recomputation and
+// dw by a per-lane bit mask over (own token, tap), so dz and dU follow.
 template <int W, bool ACT, bool VL>
 __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) void lr_bwd_cl_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ z, const bf16 *__restrict__ U,
@@ -270,12 +268,18 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) vo
         for (int e = 0; e < 4; ++e) xw[u][4 * h + e] = bf2f(xv[e]);
       }
     }
-    // document positions of the lane's own tokens t+4q+e (VL)
-    int pown[4] = {W, W, W, W};
+    // bit 8e+k: tap k of the lane's own token t+4q+e lies before its
+    // document (VL)
+    uint32_t mown = 0;
     if constexpr (VL) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pown[e] = pring[(t + 4 * q + e) & 31];
+      for (int e = 0; e < 4; ++e) {
+        const int pe = pring[(t + 4 * q + e) & 31];
+#pragma unroll
+        for (int k = 1; k < W; ++k) mown |= (k > pe ? 1u : 0u) << (8 * e + k);
+      }
     }
+    auto own_off = [&](int e, int k) { return VL && k > 0 && ((mown >> (8 * e + k)) & 1u); };
     if constexpr (ACT) {
       const s16x4 az = *reinterpret_cast<const s16x4 *>(zring + ((t + n) & 31) * ZP + 8 * q);
 #pragma unroll
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) vo
           const f32x4 wk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(az, bu[u][k], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sa[e] = fmaf((VL && k > 0 && k > pown[e]) ? 0.f : wk[e], xw[u][X0 + e - k], sa[e]);
+            sa[e] = fmaf(own_off(e, k) ? 0.f : wk[e], xw[u][X0 + e - k], sa[e]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) ds[u][e] = dyc[u][e] * silu_grad_f(sa[e]);
@@ -303,14 +307,14 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) vo
           f32x4{ds[u][0], ds[u][1], ds[u][2], ds[u][3]};
     __builtin_amdgcn_wave_barrier();
     if (st > 0) {
-      // document positions of tokens t-16+4q+i, i < W+3 (VL)
-      int psh[W + 3];
-#pragma unroll
-      for (int i = 0; i < W + 3; ++i) psh[i] = VL ? pring[(t - 16 + 4 * q + i) & 31] : W;
       s16x4 az[W];
 #pragma unroll
-      for (int k = 0; k < W; ++k)
+      for (int k = 0; k < W; ++k) {
         az[k] = *reinterpret_cast<const s16x4 *>(zring + ((t - 16 + n + k) & 31) * ZP + 8 * q);
+        // row n of the tap-k operand is token t-16+n+k: drop it where tap k
+        // reaches before that token's document (VL)
+        if (VL && k > 0 && k > pring[(t - 16 + n + k) & 31]) az[k] = s16x4{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
         float dw[4 * NDQ];
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) vo
           const f32x4 wk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(az[k], bu[u][k], f32x4{ini, ini, ini, ini}, 0, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            o[e] = fmaf((VL && k > 0 && k > psh[e + k]) ? 0.f : wk[e], dw[e + k], o[e]);
+            o[e] = fmaf(wk[e], dw[e + k], o[e]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) vo
           float pr[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            pr[e] = (VL && k > 0 && k > pown[e]) ? 0.f : ds[u][e] * xw[u][X0 + e - k];
+            pr[e] = own_off(e, k) ? 0.f : ds[u][e] * xw[u][X0 + e - k];
           const uint32_t p0 = pack_bf16x2(pr[0], pr[1]);
           const uint32_t p1 = pack_bf16x2(pr[2], pr[3]);
           bdw[k] = __builtin_bit_cast(s16x4, make_uint2(p0, p1));
