@@ -40,7 +40,9 @@ bool overlap(const Span &a, const Span &b) {
   return a.lo < b.hi && b.lo < a.hi;
 }
 
-const int64_t kMaxElems = (int64_t)1 << 62;
+// Activation tensors above 2^38 elements exceed one GPU's memory by far; the
+// bound also keeps every launch grid below 2^31 workgroups.
+const int64_t kMaxElems = (int64_t)1 << 38;
 
 // Common shape / dtype / flag checks.  On success sets *V.
 dsc_status check_common(int64_t B, int64_t T, int64_t D, int W, int H, dsc_dtype dtype,
@@ -55,7 +57,7 @@ dsc_status check_common(int64_t B, int64_t T, int64_t D, int W, int H, dsc_dtype
   if (B > INT32_MAX || T > INT32_MAX || D > INT32_MAX)
     return fail(DSC_ERR_INVALID_ARG, "B, T and D must each be below 2^31");
   if (B > 0 && T > 0 && (B * T > kMaxElems / D))
-    return fail(DSC_ERR_INVALID_ARG, "B*T*D exceeds 2^62 elements");
+    return fail(DSC_ERR_INVALID_ARG, "B*T*D exceeds 2^38 elements");
   if (W < 1 || W > 8) return fail(DSC_ERR_UNSUPPORTED, "W=%d outside 1..8", W);
   if (H < 1) return fail(DSC_ERR_INVALID_ARG, "H=%d must be >= 1", H);
   if (D % H) return fail(DSC_ERR_INVALID_ARG, "D=%lld is not a multiple of H=%d",

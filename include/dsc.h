@@ -42,7 +42,9 @@
  *                        the vector width (8 for bf16, 4 for fp32), a NULL
  *                        pointer for a non-empty tensor, a pointer not 16-byte
  *                        aligned, an output overlapping another tensor of the
- *                        call, or an element count above 2^62;
+ *                        call, or more than 2^38 elements in x (far beyond
+ *                        one GPU's memory; the bound keeps launch grids
+ *                        below 2^31 workgroups);
  *   DSC_ERR_UNSUPPORTED  W outside 1..8, R outside 1..16, an unknown flag or
  *                        dtype, or a tying factor H the kernels do not tile
  *                        (head-wise: H divides the vector width, or H is the

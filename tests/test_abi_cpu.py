@@ -104,7 +104,7 @@ INVALID, UNSUP, WS = 1, 2, 3
     (dict(H=3, D=48), UNSUP), (dict(H=24, D=48), UNSUP), (dict(H=8 * 128, D=8192), UNSUP),
     (dict(x=0), INVALID), (dict(y=0), INVALID), (dict(w=A + BIG + 2), INVALID),
     (dict(y=A + 8), INVALID), (dict(y=A + 64 * 8 * 2 - 16), INVALID),
-    (dict(B=1 << 31), INVALID),
+    (dict(B=1 << 31), INVALID), (dict(B=1 << 20, T=1 << 10, D=512), INVALID),
 ])
 def test_headwise_fwd_checks(lib, kw, code):
     if code == 0:
