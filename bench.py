@@ -205,6 +205,95 @@ def summarize_profiles(d, calls):
     print("\n".join(lines))
 
 
+def summarize_trace(d, name, title, command):
+    """profiles/<name>.md: every kernel of a `rocprofv3 --kernel-trace --stats`
+    run (its run_kernel_stats.csv under `d`) with calls and average time."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
+    lines = [f"# {title}", "", "Command (repository root, MI355X, TMPDIR=/tmp), then the summary:",
+             "", f"    rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
+             f"{command}", f"    python3 bench.py --summarize-trace <out> {name}", "",
+             "| kernel | calls | avg us | total us |", "|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        nm = r["Name"]
+        nm = nm[len("void "):] if nm.startswith("void ") else nm
+        nm = nm.split("(")[0]
+        lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e3:.1f} |")
+    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+TRACES = {
+    # name: (title, command traced)
+    "bench_all_kernels": ("Every kernel of one default benchmark run (step ops, decode steps, "
+                          "static-filter comparator, packed rows)",
+                          "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline"),
+    "mlp_rnn_kernels": ("Kernels of the MLP (head-wise H=64, B=4 T=4096 D=8192, W in 2,3,4,8) "
+                        "and linear-RNN (low-rank R=16 H=8 SiLU, B=16 T=4096 D=4608) "
+                        "configurations", "python3 bench.py --other-configs"),
+}
+
+
+def other_configs(dsc, di, torch, reps=10):
+    """fwd + bwd of the MLP and linear-RNN configurations (parity cases, not
+    the step): each op on its own input copy, median of `reps` event-timed
+    launches.  x of these shapes exceeds the last-level cache."""
+    stream = torch.cuda.current_stream()
+
+    def med(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)[reps // 2] * 1e3
+
+    out = {}
+    for W in (2, 3, 4, 8):
+        wl = di.WORKLOADS["mlp_headwise"].with_(W=W)
+        inp = di.make(wl)
+        x1, w1 = inp["x"].cuda(), inp["w"].cuda()
+        x2, w2, dy2 = inp["x"].cuda(), inp["w"].cuda(), inp["dy"].cuda()
+        del inp
+        y, dx, dw = torch.empty_like(x1), torch.empty_like(x1), torch.empty_like(w1)
+        tf = med(lambda: dsc.dsc_headwise_fwd(x1, w1, y, wl.H, True, False, stream))
+        tb = med(lambda: dsc.dsc_headwise_bwd(x2, w2, dy2, dx, dw, wl.H, True, False, stream))
+        N, D, G = wl.B * wl.T, wl.D, wl.D // wl.H
+        nb = 2 * (2 * N * D + N * G * W) + 2 * (3 * N * D + 2 * N * G * W)
+        out[f"mlp_headwise_W{W}"] = {"fwd_us": round(tf, 1), "bwd_us": round(tb, 1),
+                                     "tokens_per_s": round(N / ((tf + tb) * 1e-6), 1),
+                                     "gbps": round(nb / ((tf + tb) * 1e-6) / 1e9, 1)}
+        del x1, w1, x2, w2, dy2, y, dx, dw
+        torch.cuda.empty_cache()
+    wl = di.WORKLOADS["rnn_lowrank_silu"]
+    inp = di.make(wl)
+    x1, z1, U1 = inp["x"].cuda(), inp["z"].cuda(), inp["U"].cuda()
+    x2, z2, U2, dy2 = inp["x"].cuda(), inp["z"].cuda(), inp["U"].cuda(), inp["dy"].cuda()
+    del inp
+    y, dx, dz, dU = (torch.empty_like(x1), torch.empty_like(x1), torch.empty_like(z1),
+                     torch.empty_like(U1))
+    ws = dsc.lowrank_workspace(x2, z2, wl.W, wl.H)
+    tf = med(lambda: dsc.dsc_lowrank_fwd(x1, z1, U1, y, wl.W, wl.H, wl.residual, wl.act,
+                                         stream))
+    tb = med(lambda: dsc.dsc_lowrank_bwd(x2, z2, U2, dy2, dx, dz, dU, ws, wl.W, wl.H,
+                                         wl.residual, wl.act, stream))
+    N, D, R, GW = wl.B * wl.T, wl.D, wl.R, (wl.D // wl.H) * wl.W
+    nb = 2 * (2 * N * D + N * R + R * GW) + 2 * (3 * N * D + 2 * N * R + 2 * R * GW)
+    out["rnn_lowrank_silu"] = {"fwd_us": round(tf, 1), "bwd_us": round(tb, 1),
+                               "tokens_per_s": round(N / ((tf + tb) * 1e-6), 1),
+                               "gbps": round(nb / ((tf + tb) * 1e-6) / 1e9, 1)}
+    for v in out.values():
+        v["frac_of_peak"] = round(v["gbps"] / HBM_PEAK_GBPS, 4)
+    return out
+
+
 def static_bench(dsc, di, torch, dev, steps, per_kernel_ms):
     """The static-filter comparator at the step's shape: per-channel filters
     (H=1, the depthwise form), bf16, residual, forward and backward, each op on
@@ -370,9 +459,19 @@ def main():
                     help="run each op this many times (and a copy of known size), no timing")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="summarise the rocprofv3 runs under DIR into profiles/ (no GPU)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "NAME"),
+                    help="kernel table of one --kernel-trace --stats run into profiles/NAME.md; "
+                         "NAME is one of " + ", ".join(TRACES))
+    ap.add_argument("--other-configs", action="store_true",
+                    help="time the MLP and linear-RNN configurations instead of the step")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.profile_ops)
+        return
+    if args.summarize_trace:
+        d, name = args.summarize_trace
+        title, command = TRACES[name]
+        summarize_trace(d, name, title, command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -386,6 +485,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.other_configs:
+        print(json.dumps({"other_configs": other_configs(dsc, di, torch)}), flush=True)
+        return
     B, T, D, W = WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"]
     Hh, R, Hl = WORKLOAD["H_headwise"], WORKLOAD["R"], WORKLOAD["H_lowrank"]
     wh, wl = di.WORKLOADS["qkv_headwise"], di.WORKLOADS["qkv_lowrank"]
