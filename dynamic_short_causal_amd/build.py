@@ -87,7 +87,23 @@ def build(jobs=None):
     subprocess.run([HIPCC, "-shared", "--offload-arch=gfx950", "-fPIC", *objs, "-o", tmp],
                    check=True)
     os.replace(tmp, LIB)
+    build_c_consumer()
     return LIB
+
+
+CONSUMER_SRC = os.path.join(PKG, "examples", "c_consumer.c")
+CONSUMER = os.path.join(PKG, "examples", "c_consumer")
+
+
+def build_c_consumer():
+    """The plain C example program, built with gcc against include/dsc.h and
+    libdsc.so (found next to it at run time through its rpath)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", CONSUMER_SRC,
+           "-L", PKG, "-ldsc", "-L", "/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/..", "-Wl,-rpath,/opt/rocm/lib", "-o", CONSUMER]
+    subprocess.run(cmd, check=True)
+    return CONSUMER
 
 
 if __name__ == "__main__":
