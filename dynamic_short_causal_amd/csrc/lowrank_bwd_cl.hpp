@@ -1,11 +1,11 @@
 // lowrank_bwd_cl.hpp -- low-rank backward for per-channel filters (H = 1,
-// bf16), one channel per lane.
+// bf16, no activation), one channel per lane.
 //
 // Operation: the derivative of the low-rank dynamic short convolution (gist.science
 // summary "Dynamische Korte Convoluties Verbeteren Transformers", Methodologie >
 // Dynamische Korte Convoluties, Parametrisatie 1, and Efficiente
 // Trainingsimplementatie, bullet "Fused Low-Rank Kernel"):
-//   ds = dy (or dy * SiLU'(s)),  dx[t] = rho dy[t] + sum_k w[t+k,.,k] ds[t+k],
+//   ds = dy,  dx[t] = rho dy[t] + sum_k w[t+k,.,k] ds[t+k],
 //   dw[t,c,k] = ds[t,c] x[t-k,c],  dz = dw U^T,  dU = z^T dw.
 //
 // Layout.  A workgroup of 4 waves owns 128 channels and a chunk of tokens and
@@ -27,8 +27,11 @@
 //     lane's four values.
 // Compared with one token per lane, each element costs about half the vector-
 // ALU instructions and LDS bytes; it runs 16 % faster at the QKV shape.  Tied
-// heads (H > 1) would turn every channel into a filter slot (H times the dz/dU
-// MFMA work), so they stay on the token-per-lane kernel.
+// heads (H > 1) turn every channel into a filter slot (H times the dz/dU MFMA
+// work of per-group slots), and the SiLU recomputation needs a second set of
+// filter MFMAs and registers that drop the kernel to two waves per SIMD;
+// measured at the QKV shape, the token-per-lane kernel is as fast or faster
+// in both cases (H = 1 with SiLU: 269 against 320 us), so they use it.
 //
 // Rows past the sequence are handled by buffer resources (read as zero, not
 // written); the partials of dz (per channel block) and dU (per chunk) are the
@@ -115,20 +118,19 @@ template <int W> struct LrBwdClGeo {
 
 // Waves per SIMD: as many as the compiler fits without spilling (read off the
 // kernel resource-usage report; the register count grows with W).
-template <int W, bool ACT, bool VL>
+template <int W, bool VL>
 constexpr int lr_bwd_cl_min_waves() {
-  // the position masks of packed rows tip the two widest cases over
-  if constexpr (VL && ((ACT && W == 7) || (!ACT && W == 8))) return 1;
-  if constexpr (ACT) return W <= 7 ? 2 : 1;
-  else return W <= 4 ? 3 : 2;
+  // the position masks of packed rows tip the widest case over
+  if constexpr (VL && W == 8) return 1;
+  return W <= 4 ? 3 : 2;
 }
 
 // Packed rows (VL): a 32-entry ring of document positions.  A tap k >= 1 of a
 // token beyond its position is dropped: for dx by zeroing that token's z row
 // in the tap-k A operand (one row per lane), for the SiLU recomputation and
 // dw by a per-lane bit mask over (own token, tap), so dz and dU follow.
-template <int W, bool ACT, bool VL>
-__global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) void lr_bwd_cl_kernel(
+template <int W, bool VL>
+__global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr_bwd_cl_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ z, const bf16 *__restrict__ U,
     const bf16 *__restrict__ dy, const int32_t *__restrict__ pos, bf16 *__restrict__ dx,
     float *__restrict__ dzp, float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk,
@@ -233,19 +235,19 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) vo
     const brsrc rx = slab(x, t, T, D, D);
     zn = (bf16)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
     dyn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, coff, 0, kNT));
-    if (ACT || !halo) xn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, coff, 0, kNT));
+    if (!halo) xn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, coff, 0, kNT));
   };
   auto fill = [&](int st) {
     const int t = t0 + 16 * st;
     const bool halo = st == tiles;
-    if (ACT || !halo) *reinterpret_cast<uint4 *>(xring + ((t + cr) & 31) * XP + cv * 16) = xn;
+    if (!halo) *reinterpret_cast<uint4 *>(xring + ((t + cr) & 31) * XP + cv * 16) = xn;
     *reinterpret_cast<uint4 *>(dyslab + cr * XP + cv * 16) = dyn;
     if (z_on) reinterpret_cast<bf16 *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn;
     if (VL && tid < 16) pring[(t + tid) & 31] = pn;
   };
 
-  float dyp[NG][4] = {};
-  const float rho_tap = ACT ? 0.f : rho;
+  // ds = dy, so the residual rho dy folds into the tap-0 filter
+  const float rho_tap = rho;
   issue(0);
   for (int st = 0; st < nsteps; ++st) {
     const int t = t0 + 16 * st;
@@ -280,27 +282,10 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) vo
       }
     }
     auto own_off = [&](int e, int k) { return VL && k > 0 && ((mown >> (8 * e + k)) & 1u); };
-    if constexpr (ACT) {
-      const s16x4 az = *reinterpret_cast<const s16x4 *>(zring + ((t + n) & 31) * ZP + 8 * q);
 #pragma unroll
-      for (int u = 0; u < NG; ++u) {
-        float sa[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < NG; ++u)
 #pragma unroll
-        for (int k = 0; k < W; ++k) {
-          const f32x4 wk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(az, bu[u][k], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sa[e] = fmaf(own_off(e, k) ? 0.f : wk[e], xw[u][X0 + e - k], sa[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ds[u][e] = dyc[u][e] * silu_grad_f(sa[e]);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < NG; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ds[u][e] = dyc[u][e];
-    }
+      for (int e = 0; e < 4; ++e) ds[u][e] = dyc[u][e];
 #pragma unroll
     for (int u = 0; u < NG; ++u)
       *reinterpret_cast<f32x4 *>(dsring + (cl0[u] + n) * DSP + ((t + 4 * q) & 31) * 4) =
@@ -326,7 +311,7 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) vo
         }
         float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = ACT ? rho * dyp[u][e] : 0.f;
+        for (int e = 0; e < 4; ++e) o[e] = 0.f;
 #pragma unroll
         for (int k = 0; k < W; ++k) {
           const float ini = k == 0 ? rho_tap : 0.f;
@@ -341,10 +326,6 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, ACT, VL>())) vo
               __builtin_bit_cast(uint16_t, (__bf16)o[e]);
       }
     }
-#pragma unroll
-    for (int u = 0; u < NG; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dyp[u][e] = dyc[u][e];
     if (!halo) {
       const s16x4 azt = tr16(zring + ((t + 4 * q + (n >> 2)) & 31) * ZP + 8 * (n & 3));
       const int src = 16 * (n & 3) + 4 * q + (n >> 2);

@@ -418,8 +418,10 @@ __device__ __forceinline__ void gen_tap_init(
 
 // Three waves per SIMD where the compiler fits that without spilling, fewer
 // otherwise; the set was read off the kernel resource-usage report.
-template <typename E, int W, int GPV>
+template <typename E, int W, int GPV, bool VL>
 constexpr int lr_bwd_min_waves() {
+  // packed rows' position ring takes the per-channel W = 4 case over
+  if constexpr (VL && sizeof(E) == 2 && GPV == 8 && W == 4) return 2;
   if constexpr (sizeof(E) == 2)
     return GPV == 8 && W == 8 ? 1 : (GPV == 8 && W >= 5) || (GPV == 4 && W == 8) ? 2 : 3;
   else return GPV == 4 && W >= 7 ? 2 : 3;
@@ -429,7 +431,7 @@ constexpr int lr_bwd_min_waves() {
 // a tap k >= 1 of token t is zeroed where k > pos[t], in the filters of dx and
 // of the SiLU recomputation and in dw (hence in dz and dU).
 template <typename E, int W, int GPV, bool VL>
-__global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV>())) void lr_bwd_kernel(
+__global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) void lr_bwd_kernel(
     const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U,
     const E *__restrict__ dy, const int32_t *__restrict__ pos, E *__restrict__ dx,
     float *__restrict__ dzp, float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk,

@@ -30,29 +30,24 @@ template <typename E>
 static hipError_t launch_lr_reduce(const LrArgs &a, const LrBwdPlan &p, const float *dzp,
                                    const float *dUp);
 
-// per-channel filters in bf16: one channel per lane (lowrank_bwd_cl.hpp)
+// per-channel filters in bf16 without activation: one channel per lane
+// (lowrank_bwd_cl.hpp)
 template <int W, bool VL>
 static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
   hipStream_t s = (hipStream_t)a.stream;
   const float rho = a.residual ? 1.f : 0.f;
   const LrBwdPlan p = lr_bwd_plan(a.B, a.T, a.D, a.W, a.H, a.R, a.bf16);
-  if (p.cb != kClCB || a.H != 1) return hipErrorInvalidValue;  // the plan's channel blocks
+  if (p.cb != kClCB || a.H != 1 || a.act) return hipErrorInvalidValue;
   float *dzp = (float *)a.ws;
   float *dUp = (float *)((char *)a.ws + p.dz_part);
   const int64_t nblocks = a.B * p.nchunk * p.ncb;
   if (nblocks > 0) {
     constexpr int smem = LrBwdClGeo<W>::bytes;
     const int64_t N = a.B * a.T;
-    if (a.act)
-      hipLaunchKernelGGL((lr_bwd_cl_kernel<W, true, VL>), dim3((unsigned)nblocks),
-                         dim3(kClThreads), smem, s, (const bf16 *)a.x, (const bf16 *)a.z,
-                         (const bf16 *)a.U, (const bf16 *)a.dy, a.pos, (bf16 *)a.dx, dzp, dUp,
-                         (int)a.T, (int)a.D, a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
-    else
-      hipLaunchKernelGGL((lr_bwd_cl_kernel<W, false, VL>), dim3((unsigned)nblocks),
-                         dim3(kClThreads), smem, s, (const bf16 *)a.x, (const bf16 *)a.z,
-                         (const bf16 *)a.U, (const bf16 *)a.dy, a.pos, (bf16 *)a.dx, dzp, dUp,
-                         (int)a.T, (int)a.D, a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
+    hipLaunchKernelGGL((lr_bwd_cl_kernel<W, VL>), dim3((unsigned)nblocks), dim3(kClThreads),
+                       smem, s, (const bf16 *)a.x, (const bf16 *)a.z, (const bf16 *)a.U,
+                       (const bf16 *)a.dy, a.pos, (bf16 *)a.dx, dzp, dUp, (int)a.T, (int)a.D,
+                       a.R, (int)p.tc, (int)p.nchunk, (int)p.ncb, N, rho);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -61,7 +56,7 @@ static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
 
 template <typename E, int W, int GPV, bool VL>
 static hipError_t launch_lr_bwd(const LrArgs &a) {
-  if constexpr (sizeof(E) == 2 && GPV == 8) {  // H == 1
+  if (sizeof(E) == 2 && GPV == 8 && !a.act) {  // H == 1, no SiLU
     return launch_lr_bwd_cl<W, VL>(a);
   } else {
     hipStream_t s = (hipStream_t)a.stream;
