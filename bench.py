@@ -475,8 +475,9 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path would shard by batch or channel blocks with no exchange in the "
-              "forward; see DESIGN.md)", file=sys.stderr)
+              "(the op would shard by batch or by channel blocks, with no exchange in the "
+              "forward, so one GPU's share at its real shape is what this measures)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -19,7 +19,7 @@
  *           (static vs dynamic sum), 2. Solving the Parameter Explosion
  *           (rank-16 example, head-wise tying).
  *
- * Readings taken where the pages are silent (each one is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - taps that reach before the start of a sequence (t-k < 0) read zero;
  *     every sequence b is independent and the output has length T;
  *   - tap k = 0 multiplies the current token x_t;
