@@ -59,6 +59,8 @@ def _declare(lib):
                                   _int, _int],
         "oracle_lowrank_bwd_vl": [_dp, _dp, _dp, _ip, _dp, _dp, _dp, _dp, _i64, _i64, _i64,
                                   _int, _int, _int, _int, _int],
+        "oracle_headwise_gen_fwd": [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, _int, _int,
+                                    _int, _int],
         "oracle_static_fwd": [_dp, _dp, _dp, _i64, _i64, _i64, _int, _int, _int, _int],
         "oracle_static_bwd": [_dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _int, _int, _int,
                               _int],
@@ -270,6 +272,20 @@ class Oracle:
         self.lib.oracle_static_bwd(_p(x), _p(w), _p(dy), _p(dx), _p(dw), B, T, D, w.shape[1],
                                    H, int(residual), int(act))
         return dx, dw
+
+    # ---- filter generation fused with the convolution --------------------
+    def headwise_gen_fwd(self, x, xh, M, H, residual=False, act=False):
+        """x (B,T,D), xh (B,T,Dh), M (Dh, G*W) -> y (B,T,D) with w = xh M."""
+        x, xh, M = _c(x), _c(xh), _c(M)
+        B, T, D = x.shape
+        Dh = xh.shape[-1]
+        G = D // H
+        W = M.shape[1] // G
+        assert xh.shape == (B, T, Dh) and M.shape == (Dh, G * W)
+        y = np.empty_like(x)
+        self.lib.oracle_headwise_gen_fwd(_p(x), _p(xh), _p(M), _p(y), B, T, D, Dh, W, H,
+                                         int(residual), int(act))
+        return y
 
     # ---- packed variable-length sequences ---------------------------------
     @staticmethod

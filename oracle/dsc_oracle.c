@@ -653,3 +653,28 @@ void oracle_lowrank_bwd_vl(const double *x, const double *z, const double *U,
   free(w);
   free(gw);
 }
+
+/*
+ * Filter generation fused with the convolution (head-wise, forward).  The
+ * filter of token t is a learned linear map of a hidden state ([gist]
+ * Parametrisatie): w[b,t,:] = xh[b,t,:] M, with xh (B, T, Dh) and M (Dh, G*W)
+ * (column g*W + k), and the convolution then runs as in oracle_headwise_fwd.
+ * [wisp] Limitations names merging the convolution into the preceding matrix
+ * product as the next step for inference; the oracle simply forms w first.
+ */
+void oracle_headwise_gen_fwd(const double *x, const double *xh, const double *M, double *y,
+                             int64_t B, int64_t T, int64_t D, int64_t Dh, int W, int H,
+                             int residual, int act) {
+  int64_t G = D / H, GW = G * W, N = B * T;
+  double *w = (double *)malloc(sizeof(double) * (size_t)(N * GW));
+  if (!w) return;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t j = 0; j < GW; ++j) {
+      double a = 0.0;
+      for (int64_t k = 0; k < Dh; ++k) a += xh[n * Dh + k] * M[k * GW + j];
+      w[n * GW + j] = a;
+    }
+  oracle_headwise_fwd(x, w, y, B, T, D, W, H, residual, act);
+  free(w);
+}

@@ -535,6 +535,26 @@ def pin_varlen_finite_differences(orc):
         _close(dU, _fd(lambda a: np.sum(orc.lowrank_fwd_vl(x, z, a, pos, W, H, res, act) * dy),
                        U), rtol=1e-7, atol=1e-7, what="fd vl dU")
 
+# ---------------------------------------------------------------- generated filters
+def pin_generated_filters(orc):
+    """The fused generator equals the head-wise forward fed w = xh @ M (numpy
+    matmul), with the filter columns laid out g*W + k."""
+    rng = _rng(60)
+    for (B, T, D, Dh, W, H) in [(2, 9, 16, 12, 4, 8), (1, 5, 8, 3, 2, 8), (2, 4, 12, 7, 3, 4)]:
+        G = D // H
+        x, xh = _rand(rng, B, T, D), _rand(rng, B, T, Dh)
+        M = _rand(rng, Dh, G * W, std=0.3)
+        w = (xh.reshape(-1, Dh) @ M).reshape(B, T, G, W)
+        for res, act in ((False, False), (True, True)):
+            _close(orc.headwise_gen_fwd(x, xh, M, H, res, act), orc.headwise_fwd(x, w, H, res, act),
+                   what=f"generated filters {B,T,D,Dh,W,H}")
+    # one token, one group: y = sum_k (xh M)[k] x_{t-k}, worked by hand
+    x = np.array([[[1.0], [2.0]]])                 # B=1, T=2, D=1
+    xh = np.array([[[1.0, 0.0], [0.5, 2.0]]])      # Dh=2
+    M = np.array([[1.0, -1.0], [0.25, 3.0]])       # W=2: w_t = (xh_t0 + 0.25 xh_t1, -xh_t0 + 3 xh_t1)
+    # t=0: w = (1, -1), y = 1*1 = 1;  t=1: w = (1, 5.5), y = 1*2 + 5.5*1 = 7.5
+    _close(orc.headwise_gen_fwd(x, xh, M, 1), [[[1.0], [7.5]]], what="generated filters by hand")
+
 
 ALL_PINS = [pin_handworked, pin_width_one_is_scale, pin_silu_values,
             pin_static_filter_is_conv1d, pin_causality, pin_linearity,
@@ -543,4 +563,5 @@ ALL_PINS = [pin_handworked, pin_width_one_is_scale, pin_silu_values,
             pin_sampled_match_full, pin_decode_handworked, pin_decode_rolls_forward,
             pin_static_is_conv1d, pin_static_is_broadcast_dynamic,
             pin_static_finite_differences, pin_varlen_one_document_is_dense,
-            pin_varlen_documents_are_independent, pin_varlen_finite_differences]
+            pin_varlen_documents_are_independent, pin_varlen_finite_differences,
+            pin_generated_filters]

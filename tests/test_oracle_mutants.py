@@ -55,6 +55,8 @@ MUTANTS = {
                               "if (k < pos[n] && t - k >= 0) s += w[(n * G + g) * W + k]"),
     "varlen_dx_mask_own_pos": ("        if (k <= pos[m])\n", "        if (k <= pos[n])\n"),
     "varlen_dw_unmasked": ("        if (k <= pos[n] && tau - k >= 0)\n", "        if (tau - k >= 0)\n"),
+    "gen_M_transposed": ("for (int64_t k = 0; k < Dh; ++k) a += xh[n * Dh + k] * M[k * GW + j];",
+                         "for (int64_t k = 0; k < Dh; ++k) a += xh[n * Dh + k] * M[(j % Dh) * GW + (k % GW)];"),
     "residual_twice": ("y[n * D + c] = act_fn(s, act) + (residual ? x[n * D + c] : 0.0);\n    }\n  }\n}",
                        "y[n * D + c] = act_fn(s, act) + (residual ? 2.0 * x[n * D + c] : 0.0);\n    }\n  }\n}"),
 }
