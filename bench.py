@@ -395,6 +395,51 @@ def varlen_bench(dsc, di, torch, dev, steps, per_kernel_ms):
     return out
 
 
+def gen_bench(dsc, di, torch, dev, steps, Dh=2048):
+    """Filters generated from a hidden state xh (B, T, Dh) of a 2048-wide model
+    at the step's head-wise shape (H=16, W=4, bf16, residual), forward only:
+    the fused kernel (w = xh M on chip) against the unfused pair, a library
+    GEMM writing w (torch.matmul on hipBLASLt) then the head-wise forward
+    reading it.  Each timing reads its own copies.  Not part of the step."""
+    B, T, D, W, Hh = (WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"],
+                      WORKLOAD["H_headwise"])
+    G, N = D // Hh, B * T
+    stream = torch.cuda.current_stream()
+    mk = lambda shape, std, seed: di.randn(shape, std, seed, "bf16").to(dev)
+    x1, xh1 = mk((B, T, D), 1.0, 70), mk((B, T, Dh), 1.0, 71)
+    x2, xh2 = mk((B, T, D), 1.0, 72), mk((B, T, Dh), 1.0, 73)
+    M = mk((Dh, G * W), (0.25 / Dh) ** 0.5, 74)
+    y1, y2 = torch.empty_like(x1), torch.empty_like(x2)
+    w2 = torch.empty((B, T, G, W), dtype=torch.bfloat16, device=dev)
+
+    def fused():
+        dsc.dsc_headwise_gen_fwd(x1, xh1, M, y1, W, Hh, True, False, stream)
+
+    def unfused():
+        torch.matmul(xh2.view(N, Dh), M, out=w2.view(N, G * W))
+        dsc.dsc_headwise_fwd(x2, w2, y2, Hh, True, False, stream)
+
+    out = {}
+    for name, fn in (("fused", fused), ("unfused", unfused)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        out[f"{name}_us"] = round(sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3, 1)
+    flops = 2.0 * N * Dh * G * W
+    out["gemm_tflops_fused"] = round(flops / (out["fused_us"] * 1e-6) / 1e12, 1)
+    out["hbm_bytes_fused"] = 2 * (N * Dh + Dh * G * W + 2 * N * D)
+    out["fused_over_unfused"] = round(out["fused_us"] / out["unfused_us"], 3)
+    out["config"] = f"B={B} T={T} D={D} Dh={Dh} W={W} H={Hh}"
+    return out
+
+
 def decode_bench(dsc, di, torch, dev, iters=200):
     """One-token steps at serving batches, for head-wise H=16 and low-rank R=16
     H=1 at D=6144, W=4, bf16, residual.  Two timings of `iters` steps in a row:
@@ -582,6 +627,8 @@ def main():
     static = static_bench(dsc, di, torch, dev, args.steps, per_kernel_ms)
     print("bench: timing packed rows", file=sys.stderr, flush=True)
     varlen = varlen_bench(dsc, di, torch, dev, args.steps, per_kernel_ms)
+    print("bench: timing generated filters", file=sys.stderr, flush=True)
+    gen = gen_bench(dsc, di, torch, dev, args.steps)
 
     nbytes = algorithmic_bytes(B, T, D, W, Hh, R, Hl)
     ms_per_step = elapsed / args.steps * 1e3
@@ -627,6 +674,7 @@ def main():
         "decode": decode,
         "static_comparator": static,
         "packed_rows": varlen,
+        "generated_filters": gen,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

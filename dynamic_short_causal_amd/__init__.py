@@ -27,7 +27,7 @@ EXPORTS = ("dsc_version", "dsc_status_string", "dsc_last_error", "dsc_headwise_f
            "dsc_lowrank_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
            "dsc_decode_state", "dsc_static_fwd", "dsc_static_bwd_workspace_bytes",
            "dsc_static_bwd", "dsc_headwise_fwd_varlen", "dsc_headwise_bwd_varlen",
-           "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen")
+           "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_headwise_gen_fwd")
 
 
 class DscError(RuntimeError):
@@ -62,6 +62,7 @@ def _load():
     lib.dsc_static_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.dsc_static_bwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, ci,
                                    ci, ci, cu, vp]
+    lib.dsc_headwise_gen_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ci, ci, ci, cu, vp]
     lib.dsc_headwise_fwd_varlen.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, cu, vp]
     lib.dsc_headwise_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, ci,
                                             cu, vp]
@@ -73,7 +74,7 @@ def _load():
                  "dsc_lowrank_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
                  "dsc_decode_state", "dsc_static_fwd", "dsc_static_bwd",
                  "dsc_headwise_fwd_varlen", "dsc_headwise_bwd_varlen",
-                 "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen"):
+                 "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_headwise_gen_fwd"):
         getattr(lib, name).restype = ci
     return lib
 
@@ -306,6 +307,18 @@ def dsc_lowrank_bwd_varlen(x, z, U, pos, dy, dx, dz, dU, workspace, W, H, residu
     return dx, dz, dU
 
 
+def dsc_headwise_gen_fwd(x, xh, M, y, W, H, residual=False, act=False, stream=None):
+    """Filters generated on chip: w = xh M with xh (B, T, Dh), M (Dh, G*W)."""
+    B, T, D = x.shape
+    Dh = xh.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("xh", xh, (B, T, Dh)), ("M", M, (Dh, (D // H) * W)),
+                    ("y", y, (B, T, D))):
+        _need(t, n, s, x.dtype)
+    _check(LIB.dsc_headwise_gen_fwd(_ptr(x), _ptr(xh), _ptr(M), _ptr(y), B, T, D, Dh, W, H,
+                                    _dtype(x), _flags(residual, act), _stream(stream)))
+    return y
+
+
 # --------------------------------------------------------------- allocating forms
 def headwise_fwd(x, w, H, residual=False, act=False, stream=None):
     return dsc_headwise_fwd(x, w, torch.empty_like(x), H, residual, act, stream)
@@ -382,3 +395,7 @@ def lowrank_bwd_varlen(x, z, U, pos, dy, W, H, residual=False, act=False, worksp
         workspace = lowrank_workspace(x, z, W, H)
     return dsc_lowrank_bwd_varlen(x, z, U, pos, dy, torch.empty_like(x), torch.empty_like(z),
                                   torch.empty_like(U), workspace, W, H, residual, act, stream)
+
+
+def headwise_gen_fwd(x, xh, M, W, H, residual=False, act=False, stream=None):
+    return dsc_headwise_gen_fwd(x, xh, M, torch.empty_like(x), W, H, residual, act, stream)

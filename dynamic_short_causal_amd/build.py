@@ -19,7 +19,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsc.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dsc_abi.cpp", "headwise.hip", "decode.hip", "static.hip", "lowrank.hip",
+SOURCES = ["dsc_abi.cpp", "headwise.hip", "decode.hip", "static.hip", "gen.hip", "lowrank.hip",
            "lowrank_fwd_bf16.hip", "lowrank_bwd_bf16.hip", "lowrank_fwd_f32.hip",
            "lowrank_bwd_f32.hip", "lowrank_fwd_bf16_vl.hip", "lowrank_bwd_bf16_vl.hip",
            "lowrank_fwd_f32_vl.hip", "lowrank_bwd_f32_vl.hip"]

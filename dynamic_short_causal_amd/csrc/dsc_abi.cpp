@@ -11,6 +11,7 @@
 #include "dsc_launch.hpp"
 #include "decode_launch.hpp"
 #include "static_launch.hpp"
+#include "gen_launch.hpp"
 
 namespace {
 
@@ -421,6 +422,38 @@ dsc_status dsc_static_bwd(const void *x, const void *w, const void *dy, void *dx
   dsc::StArgs a = static_args(B, T, D, W, H, dtype, flags, stream, true);
   a.x = x; a.w = w; a.dy = dy; a.dx = dx; a.dw = dw; a.ws = workspace;
   return hip_status(dsc::static_launch(a));
+}
+
+dsc_status dsc_headwise_gen_fwd(const void *x, const void *xh, const void *M, void *y, int64_t B,
+                                int64_t T, int64_t D, int64_t Dh, int W, int H,
+                                dsc_dtype dtype, unsigned flags, void *stream) {
+  int V = 0;
+  dsc_status st = check_common(B, T, D, W, H, dtype, flags, &V);
+  if (st != DSC_OK) return st;
+  if (dtype != DSC_BF16) return fail(DSC_ERR_UNSUPPORTED, "generated filters: bf16 only");
+  if (W != 1 && W != 2 && W != 4 && W != 8)
+    return fail(DSC_ERR_UNSUPPORTED, "generated filters: W=%d not in {1, 2, 4, 8}", W);
+  if (H % 8) return fail(DSC_ERR_UNSUPPORTED, "generated filters: H=%d not a multiple of 8", H);
+  if (Dh < 64 || Dh % 64 || Dh > INT32_MAX)
+    return fail(DSC_ERR_UNSUPPORTED, "generated filters: Dh=%lld not a positive multiple of 64",
+                (long long)Dh);
+  const int64_t GW = (D / H) * W;
+  if (GW % 8)
+    return fail(DSC_ERR_UNSUPPORTED, "generated filters: G*W=%lld not a multiple of 8",
+                (long long)GW);
+  if (B > 0 && T > 0 && B * T > kMaxElems / Dh)
+    return fail(DSC_ERR_INVALID_ARG, "B*T*Dh exceeds 2^38 elements");
+  const int64_t n_act = B * T * D;
+  Span s[4] = {span("x", x, n_act, 2, false), span("xh", xh, B * T * Dh, 2, false),
+               span("M", M, Dh * GW, 2, false), span("y", y, n_act, 2, true)};
+  if ((st = check_ptrs(s, 4)) != DSC_OK) return st;
+  dsc::GenArgs a{};
+  a.x = x; a.xh = xh; a.M = M; a.y = y;
+  a.B = B; a.T = T; a.D = D; a.Dh = Dh; a.W = W; a.H = H;
+  a.residual = (flags & DSC_RESIDUAL) != 0;
+  a.act = (flags & DSC_ACT_SILU) != 0;
+  a.stream = stream;
+  return hip_status(dsc::gen_launch(a));
 }
 
 }  // extern "C"

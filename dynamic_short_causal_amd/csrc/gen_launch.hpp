@@ -1,0 +1,23 @@
+// gen_launch.hpp -- host-side arguments of the fused filter-generation kernel
+// in gen.hip (head-wise forward with w = xh M formed on chip), filled in by
+// the C ABI after its checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsc {
+
+// x, y (B, T, D); xh (B, T, Dh); M (Dh, G*W), column g*W + k; bf16 only.
+struct GenArgs {
+  const void *x, *xh, *M;
+  void *y;
+  int64_t B, T, D, Dh;
+  int W, H;
+  bool residual, act;
+  void *stream;
+};
+
+hipError_t gen_launch(const GenArgs &a);
+
+}  // namespace dsc

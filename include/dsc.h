@@ -236,6 +236,22 @@ dsc_status dsc_lowrank_bwd_varlen(const void *x, const void *z, const void *U,
                                   int64_t T, int64_t D, int W, int H, int R, dsc_dtype dtype,
                                   unsigned flags, void *stream);
 
+/*
+ * Head-wise forward with the filters generated on chip from a hidden state
+ * ([gist] Parametrisatie: the filter is a learned linear map of the hidden
+ * state; [wisp] Limitations: merging the convolution into the preceding
+ * matrix product):
+ *   w[b,t,:] = xh[b,t,:] M,  xh (B, T, Dh), M (Dh, G*W) with column g*W + k,
+ * then y exactly as dsc_headwise_fwd with that w, which never reaches device
+ * memory.  w is rounded to bf16 before use, as a stored w would be.  bf16 only;
+ * W in {1, 2, 4, 8}; H a multiple of 8; Dh a multiple of 64; G*W a multiple
+ * of 8 (else DSC_ERR_UNSUPPORTED).  Other checks and errors as for the
+ * head-wise calls.  Forward only (inference).
+ */
+dsc_status dsc_headwise_gen_fwd(const void *x, const void *xh, const void *M, void *y,
+                                int64_t B, int64_t T, int64_t D, int64_t Dh, int W, int H,
+                                dsc_dtype dtype, unsigned flags, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
