@@ -233,6 +233,10 @@ TRACES = {
     "mlp_rnn_kernels": ("Kernels of the MLP (head-wise H=64, B=4 T=4096 D=8192, W in 2,3,4,8) "
                         "and linear-RNN (low-rank R=16 H=8 SiLU, B=16 T=4096 D=4608) "
                         "configurations", "python3 bench.py --other-configs"),
+    "generated_filter_kernels": ("Kernels of the generated-filter comparison, B=8 T=2048 "
+                                 "D=6144 Dh=2048 W=4 H=16 bf16 residual: the fused kernel, "
+                                 "then the library GEMM writing w and the head-wise forward",
+                                 "python3 bench.py --generated-filters --steps 5"),
 }
 
 
@@ -398,8 +402,9 @@ def varlen_bench(dsc, di, torch, dev, steps, per_kernel_ms):
 def gen_bench(dsc, di, torch, dev, steps, Dh=2048):
     """Filters generated from a hidden state xh (B, T, Dh) of a 2048-wide model
     at the step's head-wise shape (H=16, W=4, bf16, residual), forward only:
-    the fused kernel (w = xh M on chip) against the unfused pair, a library
-    GEMM writing w (torch.matmul on hipBLASLt) then the head-wise forward
+    the fused kernel (w = xh M on chip, M passed as Mt (G*W, Dh)) against the
+    unfused pair, a library GEMM writing w (torch.matmul on hipBLASLt, timed
+    with M in both layouts and the faster kept) then the head-wise forward
     reading it.  Each timing reads its own copies.  Not part of the step."""
     B, T, D, W, Hh = (WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"],
                       WORKLOAD["H_headwise"])
@@ -409,18 +414,27 @@ def gen_bench(dsc, di, torch, dev, steps, Dh=2048):
     x1, xh1 = mk((B, T, D), 1.0, 70), mk((B, T, Dh), 1.0, 71)
     x2, xh2 = mk((B, T, D), 1.0, 72), mk((B, T, Dh), 1.0, 73)
     M = mk((Dh, G * W), (0.25 / Dh) ** 0.5, 74)
+    Mt = M.t().contiguous()
     y1, y2 = torch.empty_like(x1), torch.empty_like(x2)
     w2 = torch.empty((B, T, G, W), dtype=torch.bfloat16, device=dev)
 
     def fused():
-        dsc.dsc_headwise_gen_fwd(x1, xh1, M, y1, W, Hh, True, False, stream)
+        dsc.dsc_headwise_gen_fwd(x1, xh1, Mt, y1, W, Hh, True, False, stream)
 
-    def unfused():
+    def unfused_nn():
         torch.matmul(xh2.view(N, Dh), M, out=w2.view(N, G * W))
         dsc.dsc_headwise_fwd(x2, w2, y2, Hh, True, False, stream)
 
+    def unfused_nt():
+        torch.matmul(xh2.view(N, Dh), Mt.t(), out=w2.view(N, G * W))
+        dsc.dsc_headwise_fwd(x2, w2, y2, Hh, True, False, stream)
+
+    def gemm_only():
+        torch.matmul(xh2.view(N, Dh), M, out=w2.view(N, G * W))
+
     out = {}
-    for name, fn in (("fused", fused), ("unfused", unfused)):
+    for name, fn in (("fused", fused), ("unfused_M", unfused_nn), ("unfused_Mt", unfused_nt),
+                     ("library_gemm_alone", gemm_only)):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -432,6 +446,7 @@ def gen_bench(dsc, di, torch, dev, steps, Dh=2048):
             b.record(stream)
         torch.cuda.synchronize()
         out[f"{name}_us"] = round(sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3, 1)
+    out["unfused_us"] = min(out["unfused_M_us"], out["unfused_Mt_us"])
     flops = 2.0 * N * Dh * G * W
     out["gemm_tflops_fused"] = round(flops / (out["fused_us"] * 1e-6) / 1e12, 1)
     out["hbm_bytes_fused"] = 2 * (N * Dh + Dh * G * W + 2 * N * D)
@@ -509,6 +524,8 @@ def main():
                          "NAME is one of " + ", ".join(TRACES))
     ap.add_argument("--other-configs", action="store_true",
                     help="time the MLP and linear-RNN configurations instead of the step")
+    ap.add_argument("--generated-filters", action="store_true",
+                    help="time only the generated-filter comparison (fused against unfused)")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.profile_ops)
@@ -533,6 +550,10 @@ def main():
     torch.cuda.set_device(dev)
     if args.other_configs:
         print(json.dumps({"other_configs": other_configs(dsc, di, torch)}), flush=True)
+        return
+    if args.generated_filters:
+        print(json.dumps({"generated_filters": gen_bench(dsc, di, torch, dev, args.steps)}),
+              flush=True)
         return
     B, T, D, W = WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"]
     Hh, R, Hl = WORKLOAD["H_headwise"], WORKLOAD["R"], WORKLOAD["H_lowrank"]

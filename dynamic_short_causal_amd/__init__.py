@@ -307,14 +307,15 @@ def dsc_lowrank_bwd_varlen(x, z, U, pos, dy, dx, dz, dU, workspace, W, H, residu
     return dx, dz, dU
 
 
-def dsc_headwise_gen_fwd(x, xh, M, y, W, H, residual=False, act=False, stream=None):
-    """Filters generated on chip: w = xh M with xh (B, T, Dh), M (Dh, G*W)."""
+def dsc_headwise_gen_fwd(x, xh, Mt, y, W, H, residual=False, act=False, stream=None):
+    """Filters generated on chip: w = xh M with xh (B, T, Dh) and M given
+    transposed, Mt (G*W, Dh) (a linear layer's weight layout)."""
     B, T, D = x.shape
     Dh = xh.shape[-1]
-    for n, t, s in (("x", x, (B, T, D)), ("xh", xh, (B, T, Dh)), ("M", M, (Dh, (D // H) * W)),
+    for n, t, s in (("x", x, (B, T, D)), ("xh", xh, (B, T, Dh)), ("Mt", Mt, ((D // H) * W, Dh)),
                     ("y", y, (B, T, D))):
         _need(t, n, s, x.dtype)
-    _check(LIB.dsc_headwise_gen_fwd(_ptr(x), _ptr(xh), _ptr(M), _ptr(y), B, T, D, Dh, W, H,
+    _check(LIB.dsc_headwise_gen_fwd(_ptr(x), _ptr(xh), _ptr(Mt), _ptr(y), B, T, D, Dh, W, H,
                                     _dtype(x), _flags(residual, act), _stream(stream)))
     return y
 
@@ -397,5 +398,5 @@ def lowrank_bwd_varlen(x, z, U, pos, dy, W, H, residual=False, act=False, worksp
                                   torch.empty_like(U), workspace, W, H, residual, act, stream)
 
 
-def headwise_gen_fwd(x, xh, M, W, H, residual=False, act=False, stream=None):
-    return dsc_headwise_gen_fwd(x, xh, M, torch.empty_like(x), W, H, residual, act, stream)
+def headwise_gen_fwd(x, xh, Mt, W, H, residual=False, act=False, stream=None):
+    return dsc_headwise_gen_fwd(x, xh, Mt, torch.empty_like(x), W, H, residual, act, stream)

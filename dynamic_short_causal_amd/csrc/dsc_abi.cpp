@@ -424,7 +424,7 @@ dsc_status dsc_static_bwd(const void *x, const void *w, const void *dy, void *dx
   return hip_status(dsc::static_launch(a));
 }
 
-dsc_status dsc_headwise_gen_fwd(const void *x, const void *xh, const void *M, void *y, int64_t B,
+dsc_status dsc_headwise_gen_fwd(const void *x, const void *xh, const void *Mt, void *y, int64_t B,
                                 int64_t T, int64_t D, int64_t Dh, int W, int H,
                                 dsc_dtype dtype, unsigned flags, void *stream) {
   int V = 0;
@@ -445,10 +445,10 @@ dsc_status dsc_headwise_gen_fwd(const void *x, const void *xh, const void *M, vo
     return fail(DSC_ERR_INVALID_ARG, "B*T*Dh exceeds 2^38 elements");
   const int64_t n_act = B * T * D;
   Span s[4] = {span("x", x, n_act, 2, false), span("xh", xh, B * T * Dh, 2, false),
-               span("M", M, Dh * GW, 2, false), span("y", y, n_act, 2, true)};
+               span("Mt", Mt, Dh * GW, 2, false), span("y", y, n_act, 2, true)};
   if ((st = check_ptrs(s, 4)) != DSC_OK) return st;
   dsc::GenArgs a{};
-  a.x = x; a.xh = xh; a.M = M; a.y = y;
+  a.x = x; a.xh = xh; a.Mt = Mt; a.y = y;
   a.B = B; a.T = T; a.D = D; a.Dh = Dh; a.W = W; a.H = H;
   a.residual = (flags & DSC_RESIDUAL) != 0;
   a.act = (flags & DSC_ACT_SILU) != 0;

@@ -1,6 +1,8 @@
 // gen.hip -- head-wise dynamic short convolution with the filters generated on
 // chip from a hidden state: w[n, :] = xh[n, :] M, then y as in the head-wise
-// forward.  w never reaches device memory.
+// forward.  w never reaches device memory.  M arrives transposed, as Mt
+// (G*W, Dh) (the weight layout of a linear layer), so that both GEMM operands
+// are contiguous along the reduction index Dh.
 //
 // Operation: gist.science summary "Dynamische Korte Convoluties Verbeteren
 // Transformers", Methodologie > Dynamische Korte Convoluties (bullets
@@ -9,19 +11,28 @@
 // "Dynamic Short Convolutions", Limitations, names merging the convolution into
 // the preceding matrix product as the next step for inference.
 //
-// Mapping: a workgroup of 4 waves owns 64 tokens (flattened b*T + t) and 256
-// filter columns, i.e. 256 / W groups of H channels.
-//   * GEMM: the 64 x 256 tile of w = xh M accumulates over Dh in K-tiles of
-//     64 staged in LDS (xh rows, M rows), with the next tile's loads held in
-//     registers while the current one is consumed.  Each wave computes 64 x 64
-//     with 16x16x32 bf16 MFMAs: A fragments are 16-byte row reads, B fragments
-//     come from the transposing LDS read (ds_read_b64_tr_b16).
+// Mapping: a workgroup of 4 waves owns 128 tokens (flattened b*T + t) and NC
+// = 128 filter columns (the tile code also takes 192 and 256), i.e. NC / W
+// groups of H channels.  Workgroups of one token tile are adjacent in launch
+// order, so its xh rows are fetched from device memory about once.
+//   * GEMM: the 128 x NC tile of w = xh M accumulates over Dh in K-tiles of
+//     32 through a ring of 3 LDS stages.  Tiles (128 xh rows and NC Mt rows of
+//     64 bytes) are copied from device memory straight into LDS
+//     (global_load_lds_dwordx4), two tiles ahead of the one being multiplied,
+//     with one barrier per K-tile.  The waves form a 2 x 2 grid of 64 x NC/2
+//     sub-tiles computed with 16x16x32 bf16 MFMAs whose A and B fragments are
+//     both 16-byte LDS reads.  Rows are XOR-swizzled in 16-byte granules so
+//     that these reads are free of bank conflicts; the swizzle is applied on
+//     the device-memory side of the copy, since a copy instruction fills
+//     1 KiB of LDS in lane order.
 //   * Epilogue: the tile is rounded to bf16 (the precision a stored w would
-//     have) into LDS; threads then walk (channel vector, token segment) items:
-//     the causal window of x comes from device memory (rows of the same
-//     sequence only), the taps from the LDS tile, and y goes out in 16-byte
-//     stores.  A token tile may span two sequences; the window restarts at
-//     every sequence start.
+//     have) into LDS; each thread then owns one 16-byte channel vector and a
+//     run of consecutive tokens, keeping the causal window in registers with
+//     8 rows of x in flight, and stores y in 16-byte non-temporal writes.  A
+//     token tile may span sequences; the window restarts at every sequence
+//     start.
+// Token rows past the end and filter columns past G*W are read clamped to the
+// last valid row / column: they only feed w entries that are never used.
 #include "dsc_device.hpp"
 #include "gen_launch.hpp"
 
@@ -29,196 +40,283 @@ namespace dsc {
 
 namespace {
 
-typedef short s16x4g __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8g __attribute__((ext_vector_type(8)));
 typedef float f32x4g __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4g lds_s16x4g;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kGenThreads = 256;
-constexpr int kGT = 64;                    // tokens per workgroup
-constexpr int kGC = 256;                   // filter columns per workgroup
-constexpr int kGK = 64;                    // K-tile
-constexpr int kAP = kGK * 2 + 16;          // A tile row pitch (bytes)
-constexpr int kBP = kGC * 2 + 32;          // B tile row pitch: rows 4 apart hit distinct banks
-constexpr int kWP = kGC * 2 + 16;          // w tile row pitch
-constexpr int kOffB = kGT * kAP;           // B tile after the A tile
-constexpr int kLdsBytes = kOffB + kGK * kBP;
-static_assert(kGT * kWP <= kGK * kBP, "the w tile reuses the B tile");
+constexpr int kGT = 128;                   // tokens per workgroup
+constexpr int kGK = 32;                    // K-tile
+constexpr int kStages = 3;                 // LDS ring depth
+constexpr int kABytes = kGT * kGK * 2;     // A tile: 128 rows of 64 bytes
+constexpr int kUN = 8;                     // x rows in flight per thread (epilogue)
 
-__device__ __forceinline__ s16x4g tr16g(const unsigned char *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4g *)(__attribute__((address_space(3))) char *)(uintptr_t)p);
+template <int NC> struct GenTile {
+  static_assert(NC == 128 || NC == 192 || NC == 256, "column tile");
+  static constexpr int Stage = (kGT + NC) * kGK * 2;   // A rows, then B rows
+  static constexpr int WP = NC * 2 + 16;               // w tile row pitch (bytes)
+  static constexpr int Lds = kStages * Stage > kGT * WP ? kStages * Stage : kGT * WP;
+  static constexpr int NBI = NC / 64;                  // B copies per wave per stage
+  static constexpr int NI = 2 + NBI;                   // copies per wave per stage
+  static constexpr int CB = NC / 32;                   // 16-column blocks per wave
+};
+
+// Granule swizzle of a 64-byte tile row r (4 granules of 8 bf16 along k): a
+// 16-lane group reads granule q of 16 consecutive rows, and the XOR puts
+// those reads on 16 distinct 4-bank windows.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+// 16 bytes per lane from device memory into LDS at dst + 16 * lane (dst is
+// wave-uniform).
+__device__ __forceinline__ void copy_lds16(const void *src, unsigned char *dst) {
+  __builtin_amdgcn_global_load_lds(
+      src, (lds_void *)(__attribute__((address_space(3))) char *)(uintptr_t)dst, 16, 0, 0);
+}
+
+// Wait until at most N of this wave's copies are in flight (vmcnt), leaving
+// the other counters alone.
+template <int N> __device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders LDS accesses but leaves device-memory copies
+// in flight (a full __syncthreads would also drain those).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 }  // namespace
 
+// ---- GEMM of one 128 x NC tile of w, by waves 0..3 of the workgroup -------
+// The ring of kStages stages starts at `stages`; one lds_barrier per K-tile,
+// nkt = Dh / 32 in all.  On return every wave's accumulators hold its
+// 64 x NC/2 sub-tile: token wm*64 + 16r + 4q + e, column wn*NC/2 + 16c + j.
+template <int NC>
+__device__ __forceinline__ void gen_gemm(unsigned char *stages, const bf16 *__restrict__ xh,
+                                         const bf16 *__restrict__ Mt, int64_t n0, int col0,
+                                         int64_t N, int Dh, int GW, int wave, int lane,
+                                         f32x4g (&acc)[4][GenTile<NC>::CB]) {
+  using Tl = GenTile<NC>;
+  const int q = lane >> 4, j = lane & 15, wm = wave >> 1, wn = wave & 1;
+  // copy sources.  A copy i of a wave fills tile rows 16 (2 wave + i) .. +15,
+  // B copy i rows 16 (wave NBI + i) .. +15; lane l fills granule l & 3 of row
+  // l >> 2 with the granule of k that the swizzle puts there.
+  const int crow = lane >> 2, cgr = 8 * ((lane & 3) ^ swz(crow));
+  const bf16 *asrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t n = min(n0 + (2 * wave + i) * 16 + crow, N - 1);
+    asrc[i] = xh + n * Dh + cgr;
+  }
+  const bf16 *bsrc[Tl::NBI];
+#pragma unroll
+  for (int i = 0; i < Tl::NBI; ++i) {
+    const int col = min(col0 + (wave * Tl::NBI + i) * 16 + crow, GW - 1);
+    bsrc[i] = Mt + (int64_t)col * Dh + cgr;
+  }
+  auto issue = [&](int kt, int st) {
+    unsigned char *S = stages + st * Tl::Stage;
+    const int k0 = kt * kGK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) copy_lds16(asrc[i] + k0, S + 1024 * (2 * wave + i));
+#pragma unroll
+    for (int i = 0; i < Tl::NBI; ++i)
+      copy_lds16(bsrc[i] + k0, S + kABytes + 1024 * (wave * Tl::NBI + i));
+  };
+
+  // per-lane LDS read offsets inside a stage: fragment row 16 m + j, granule
+  // q (k = 8q .. 8q+7); the swizzle depends on j only
+  const int foff = j * 64 + 16 * (q ^ (j >> 2));
+  const int aoff = wm * 64 * 64 + foff;
+  const int boff = kABytes + wn * (NC / 2) * 64 + foff;
+
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < Tl::CB; ++c) acc[r][c] = f32x4g{0.f, 0.f, 0.f, 0.f};
+
+  const int nkt = Dh / kGK;
+  issue(0, 0);
+  if (nkt > 1) issue(1, 1);
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 1 < nkt) wait_copies<Tl::NI>();
+    else wait_copies<0>();
+    // tile kt is in LDS for every wave, and every wave is done with the stage
+    // the next copy overwrites (read in the previous K-tile)
+    lds_barrier();
+    if (kt + 2 < nkt) issue(kt + 2, (kt + 2) % kStages);
+    const unsigned char *S = stages + (kt % kStages) * Tl::Stage;
+    bf16x8g a[4], b[Tl::CB];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      a[r] = __builtin_bit_cast(bf16x8g,
+                                *reinterpret_cast<const uint4 *>(S + aoff + 1024 * r));
+#pragma unroll
+    for (int c = 0; c < Tl::CB; ++c)
+      b[c] = __builtin_bit_cast(bf16x8g,
+                                *reinterpret_cast<const uint4 *>(S + boff + 1024 * c));
+#pragma unroll
+    for (int c = 0; c < Tl::CB; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], b[c], acc[r][c], 0, 0, 0);
+  }
+}
+
+// The accumulators of gen_gemm, rounded to bf16, into a w tile of 128 rows of
+// pitch WP bytes (row = token of the tile, column = filter column g*W + k).
+template <int NC>
+__device__ __forceinline__ void gen_store_w(unsigned char *wt, int wave, int lane,
+                                            const f32x4g (&acc)[4][GenTile<NC>::CB]) {
+  using Tl = GenTile<NC>;
+  const int q = lane >> 4, j = lane & 15, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < Tl::CB; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<uint16_t *>(wt + (wm * 64 + 16 * r + 4 * q + e) * Tl::WP +
+                                      (wn * (NC / 2) + 16 * c + j) * 2) =
+            __builtin_bit_cast(uint16_t, (__bf16)acc[r][c][e]);
+}
+
+// Segments of a column block's convolution: nv vectors of 8 channels, each
+// token run `seg` = 128 / nseg long, nseg a power of two with nseg * nv <=
+// threads and seg >= minseg.
+__host__ __device__ __forceinline__ int gen_nseg(int nv, int threads, int minseg) {
+  int nseg = 1;
+  while (2 * nseg * nv <= threads && kGT / (2 * nseg) >= minseg) nseg *= 2;
+  return nseg;
+}
+
+// Output of one token from its causal window win[k] = x_{t-k} and its taps.
 template <int W, bool ACT>
-__global__ __launch_bounds__(kGenThreads) void gen_fwd_kernel(
-    const bf16 *__restrict__ x, const bf16 *__restrict__ xh, const bf16 *__restrict__ M,
+__device__ __forceinline__ uint4 gen_conv_out(const float (&win)[W][8], const float (&taps)[W],
+                                              float rho) {
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) s = fmaf(taps[k], win[k][i], s);
+    if constexpr (ACT) s = silu_f(s);
+    o[i] = fmaf(rho, win[0][i], s);
+  }
+  return pack<bf16>(o);
+}
+
+// ---------------------------------------------------------------------------
+// The kernel: GEMM of the tile, then its convolution, by all 4 waves.
+// ---------------------------------------------------------------------------
+template <int W, int NC, bool ACT>
+__global__ __launch_bounds__(kGenThreads, 2) void gen_fwd_kernel(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ xh, const bf16 *__restrict__ Mt,
     bf16 *__restrict__ y, int64_t N, int T, int D, int Dh, int H, int GW, int ncb, float rho) {
-  constexpr int GB = kGC / W;  // groups per workgroup
-  extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char *At = smem, *Bt = smem + kOffB;
-  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, j = lane & 15;
+  using Tl = GenTile<NC>;
+  constexpr int GB = NC / W;  // groups per workgroup
+  __shared__ __align__(16) unsigned char smem[Tl::Lds];
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cb = blockIdx.x % ncb;
   const int64_t n0 = (int64_t)(blockIdx.x / ncb) * kGT;
-  const int col0 = cb * kGC;  // first filter column of the block
 
-  // staging roles: A: 2 vectors (rows ar, ar + 32); B: 8 vectors (rows br + 8i)
-  const int ar = tid >> 3, av = tid & 7;
-  const int br = tid >> 5, bv = tid & 31;
-  const bool bcol_ok = col0 + bv * 8 < GW;  // GW is a multiple of 8
-  uint4 ra[2], rb[8];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t n = n0 + ar + 32 * i;
-      ra[i] = n < N ? ld16nt(xh + n * Dh + k0 + av * 8) : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      rb[i] = bcol_ok ? ld16(M + (int64_t)(k0 + br + 8 * i) * GW + col0 + bv * 8)
-                      : make_uint4(0u, 0u, 0u, 0u);
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<uint4 *>(At + (ar + 32 * i) * kAP + av * 16) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint4 *>(Bt + (br + 8 * i) * kBP + bv * 16) = rb[i];
-  };
-
-  f32x4g acc[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = f32x4g{0.f, 0.f, 0.f, 0.f};
-
-  const int nkt = Dh / kGK;
-  load_tile(0);
-  store_tile();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) load_tile((kt + 1) * kGK);
-#pragma unroll
-    for (int ks = 0; ks < kGK / 32; ++ks) {
-      bf16x8g a[4], b[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)  // rows 16r + j, k = 32 ks + 8q .. +7
-        a[r] = __builtin_bit_cast(bf16x8g, *reinterpret_cast<const uint4 *>(
-                                               At + (16 * r + j) * kAP + (32 * ks + 8 * q) * 2));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {  // k rows 32 ks + 8q .. +7 of column 64 wave + 16 c + j
-        const int c0 = 64 * wave + 16 * c;
-        const unsigned char *p0 = Bt + (32 * ks + 8 * q + (j >> 2)) * kBP + (c0 + 4 * (j & 3)) * 2;
-        const s16x4g lo = tr16g(p0), hi = tr16g(p0 + 4 * kBP);
-        const s16x4g v[2] = {lo, hi};
-        b[c] = __builtin_bit_cast(bf16x8g, v);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], b[c], acc[r][c], 0, 0, 0);
-    }
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      store_tile();
-      __syncthreads();
-    }
-  }
-
-  // w tile (bf16) into the B region: token 16r + 4q + e, column 64 wave + 16c + j
-  unsigned char *Wt = Bt;
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<uint16_t *>(Wt + (16 * r + 4 * q + e) * kWP +
-                                      (64 * wave + 16 * c + j) * 2) =
-            __builtin_bit_cast(uint16_t, (__bf16)acc[r][c][e]);
+  f32x4g acc[4][Tl::CB];
+  gen_gemm<NC>(smem, xh, Mt, n0, cb * NC, N, Dh, GW, wave, lane, acc);
+  lds_barrier();  // every wave is done with the last stage
+  gen_store_w<NC>(smem, wave, lane, acc);
   __syncthreads();
 
-  // convolution: items (channel vector v, token segment s)
-  const int ch0 = cb * GB * H;                 // first channel of the block
-  const int nv = min(GB * H, D - ch0) / 8;     // channel vectors of the block
-  int nseg = 1;  // a power of two, so the segments tile the 64 tokens exactly
-  while (2 * nseg * nv <= kGenThreads && 2 * nseg <= kGT) nseg *= 2;
-  const int seg = kGT / nseg;
-  for (int item = tid; item < nv * nseg; item += kGenThreads) {
+  // convolution: items (channel vector v, token segment)
+  const int ch0 = cb * GB * H;              // first channel of the block
+  const int nv = min(GB * H, D - ch0) / 8;  // channel vectors of the block
+  const int seg = kGT / gen_nseg(nv, kGenThreads, kUN);
+  for (int item = tid; item < nv * (kGT / seg); item += kGenThreads) {
     const int v = item % nv, sgi = item / nv;
     const int c = ch0 + v * 8;
-    const int gl = (c / H) - cb * GB;          // group inside the block
+    const int gl = c / H - cb * GB;  // group inside the block
     const int tl0 = sgi * seg;
+    if (n0 + tl0 >= N) continue;
+    int t = (int)((n0 + tl0) % T);
     float win[W][8];
     // the window before the segment's first token (same sequence only)
-    {
-      const int64_t n = n0 + tl0;
-      const int t = (int)(n % T);
 #pragma unroll
-      for (int k = 1; k < W; ++k) {
-        if (t - k >= 0 && n < N) {
-          unpack<bf16>(ld16(x + (n - k) * D + c), win[k - 1]);
-        } else {
+    for (int k = 1; k < W; ++k) {
+      if (t - k >= 0) {
+        unpack<bf16>(ld16(x + (n0 + tl0 - k) * D + c), win[k - 1]);
+      } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) win[k - 1][i] = 0.f;
-        }
+        for (int i = 0; i < 8; ++i) win[k - 1][i] = 0.f;
       }
     }
-    for (int tl = tl0; tl < tl0 + seg; ++tl) {
-      const int64_t n = n0 + tl;
-      if (n >= N) break;
-      if (n % T == 0) {  // a sequence starts: nothing before it
+    for (int tl = tl0; tl < tl0 + seg; tl += kUN) {
+      uint4 xr[kUN];
 #pragma unroll
-        for (int k = 0; k < W; ++k)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) win[k][i] = 0.f;
+      for (int u = 0; u < kUN; ++u) {
+        const int64_t n = n0 + tl + u;
+        xr[u] = n < N ? ld16nt(x + n * D + c) : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
-      for (int k = W - 1; k > 0; --k)
+      for (int u = 0; u < kUN; ++u) {
+        const int64_t n = n0 + tl + u;
+        if (n >= N) break;
+        if (t == 0) {  // a sequence starts: nothing before it
 #pragma unroll
-        for (int i = 0; i < 8; ++i) win[k][i] = win[k - 1][i];
-      unpack<bf16>(ld16nt(x + n * D + c), win[0]);
-      float taps[W];
-      unpack_row<bf16, W>(ld_row<bf16, W>(reinterpret_cast<const bf16 *>(Wt + tl * kWP) + gl * W),
-                          taps);
-      float o[8];
+          for (int k = 0; k < W; ++k)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float s = 0.f;
+            for (int i = 0; i < 8; ++i) win[k][i] = 0.f;
+        }
 #pragma unroll
-        for (int k = 0; k < W; ++k) s = fmaf(taps[k], win[k][i], s);
-        if constexpr (ACT) s = silu_f(s);
-        o[i] = fmaf(rho, win[0][i], s);
+        for (int k = W - 1; k > 0; --k)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) win[k][i] = win[k - 1][i];
+        unpack<bf16>(xr[u], win[0]);
+        float taps[W];
+        unpack_row<bf16, W>(
+            ld_row<bf16, W>(reinterpret_cast<const bf16 *>(smem + (tl + u) * Tl::WP) + gl * W),
+            taps);
+        st16nt(y + n * D + c, gen_conv_out<W, ACT>(win, taps, rho));
+        if (++t == T) t = 0;
       }
-      st16nt(y + n * D + c, pack<bf16>(o));
     }
   }
 }
 
-template <int W>
-static hipError_t launch_gen(const GenArgs &a) {
-  const int64_t N = a.B * a.T;
-  if (N == 0) return hipSuccess;
-  const int G = (int)(a.D / a.H), GW = G * a.W;
-  const int ncb = (GW + kGC - 1) / kGC;
+namespace {
+
+template <int W, int NC>
+hipError_t launch_gen_nc(const GenArgs &a, int64_t N, int GW) {
+  const int ncb = (GW + NC - 1) / NC;
   const int64_t nblocks = (N + kGT - 1) / kGT * ncb;
+  if (nblocks > INT32_MAX) return hipErrorInvalidValue;
   const float rho = a.residual ? 1.f : 0.f;
   hipStream_t s = (hipStream_t)a.stream;
   if (a.act)
-    hipLaunchKernelGGL((gen_fwd_kernel<W, true>), dim3((unsigned)nblocks), dim3(kGenThreads),
-                       kLdsBytes, s, (const bf16 *)a.x, (const bf16 *)a.xh, (const bf16 *)a.M,
+    hipLaunchKernelGGL((gen_fwd_kernel<W, NC, true>), dim3((unsigned)nblocks), dim3(kGenThreads),
+                       0, s, (const bf16 *)a.x, (const bf16 *)a.xh, (const bf16 *)a.Mt,
                        (bf16 *)a.y, N, (int)a.T, (int)a.D, (int)a.Dh, a.H, GW, ncb, rho);
   else
-    hipLaunchKernelGGL((gen_fwd_kernel<W, false>), dim3((unsigned)nblocks), dim3(kGenThreads),
-                       kLdsBytes, s, (const bf16 *)a.x, (const bf16 *)a.xh, (const bf16 *)a.M,
+    hipLaunchKernelGGL((gen_fwd_kernel<W, NC, false>), dim3((unsigned)nblocks), dim3(kGenThreads),
+                       0, s, (const bf16 *)a.x, (const bf16 *)a.xh, (const bf16 *)a.Mt,
                        (bf16 *)a.y, N, (int)a.T, (int)a.D, (int)a.Dh, a.H, GW, ncb, rho);
   return hipGetLastError();
 }
+
+// Column tile 128: three workgroups fit a CU (48 KiB of LDS, about 110
+// VGPRs), and on MI355X at B=8 T=2048 D=6144 Dh=2048 W=4 H=16 it beats the
+// wider tiles (194 us against 219 us for 192 and 218 us for 256 columns),
+// whose GEMM alone is faster (113 us for 256 against 130 us for 128) but
+// which keep two workgroups per CU, so fewer GEMM and convolution phases of
+// different workgroups overlap.
+template <int W>
+hipError_t launch_gen(const GenArgs &a) {
+  const int64_t N = a.B * a.T;
+  if (N == 0) return hipSuccess;
+  return launch_gen_nc<W, 128>(a, N, (int)(a.D / a.H) * a.W);
+}
+
+}  // namespace
 
 hipError_t gen_launch(const GenArgs &a) {
   switch (a.W) {

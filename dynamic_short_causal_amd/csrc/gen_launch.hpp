@@ -8,9 +8,10 @@
 
 namespace dsc {
 
-// x, y (B, T, D); xh (B, T, Dh); M (Dh, G*W), column g*W + k; bf16 only.
+// x, y (B, T, D); xh (B, T, Dh); Mt (G*W, Dh): row g*W + k holds column
+// g*W + k of M; bf16 only.
 struct GenArgs {
-  const void *x, *xh, *M;
+  const void *x, *xh, *Mt;
   void *y;
   int64_t B, T, D, Dh;
   int W, H;

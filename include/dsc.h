@@ -243,12 +243,14 @@ dsc_status dsc_lowrank_bwd_varlen(const void *x, const void *z, const void *U,
  * matrix product):
  *   w[b,t,:] = xh[b,t,:] M,  xh (B, T, Dh), M (Dh, G*W) with column g*W + k,
  * then y exactly as dsc_headwise_fwd with that w, which never reaches device
- * memory.  w is rounded to bf16 before use, as a stored w would be.  bf16 only;
+ * memory.  M is passed transposed, as Mt (G*W, Dh) row-major: row g*W + k
+ * holds column g*W + k of M (the weight layout of a linear layer from Dh to
+ * G*W features), so that both operands are contiguous along Dh.  w is rounded to bf16 before use, as a stored w would be.  bf16 only;
  * W in {1, 2, 4, 8}; H a multiple of 8; Dh a multiple of 64; G*W a multiple
  * of 8 (else DSC_ERR_UNSUPPORTED).  Other checks and errors as for the
  * head-wise calls.  Forward only (inference).
  */
-dsc_status dsc_headwise_gen_fwd(const void *x, const void *xh, const void *M, void *y,
+dsc_status dsc_headwise_gen_fwd(const void *x, const void *xh, const void *Mt, void *y,
                                 int64_t B, int64_t T, int64_t D, int64_t Dh, int W, int H,
                                 dsc_dtype dtype, unsigned flags, void *stream);
 

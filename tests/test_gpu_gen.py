@@ -24,10 +24,15 @@ def inputs(B, T, D, Dh, W, H, seed):
     return x, xh, M
 
 
+def mt(M):
+    """M (Dh, G*W) as the kernel takes it: transposed, (G*W, Dh), on the GPU."""
+    return M.t().contiguous().to(gu.dev())
+
+
 def run_case(dsc, orc, B, T, D, Dh, W, H, residual, act, seed):
     gu.say(f"  gen B={B} T={T} D={D} Dh={Dh} W={W} H={H} res={residual} act={act}")
     x, xh, M = inputs(B, T, D, Dh, W, H, seed)
-    y = dsc.headwise_gen_fwd(x.to(gu.dev()), xh.to(gu.dev()), M.to(gu.dev()), W, H, residual, act)
+    y = dsc.headwise_gen_fwd(x.to(gu.dev()), xh.to(gu.dev()), mt(M), W, H, residual, act)
     torch.cuda.synchronize()
     yo = orc.headwise_gen_fwd(gu.f64(x), gu.f64(xh), gu.f64(M), H, residual, act)
     gu.check("y", y, yo, torch.bfloat16, "y")
@@ -35,7 +40,7 @@ def run_case(dsc, orc, B, T, D, Dh, W, H, residual, act, seed):
 
 @pytest.mark.parametrize("W", [1, 2, 4, 8])
 def test_widths(dsc, orc, W):
-    # 2 sequences of 100 tokens: token tiles of 64 cross the sequence boundary
+    # 2 sequences of 100 tokens: the 128-token tile crosses the sequence boundary
     run_case(dsc, orc, 2, 100, 1024, 128, W, 16, True, False, 9900 + W)
 
 
@@ -45,7 +50,7 @@ def test_tying(dsc, orc, H):
 
 
 def test_channel_blocks_and_ragged(dsc, orc):
-    """Six full 256-column blocks; then a last block holding one group."""
+    """Twelve full 128-column blocks; then a last block holding one group."""
     run_case(dsc, orc, 1, 130, 6144, 192, 4, 16, True, True, 9920)
     run_case(dsc, orc, 2, 33, 1032, 64, 8, 8, True, False, 9921)
 
@@ -55,20 +60,48 @@ def test_one_token_sequences_and_short_batches(dsc, orc):
     run_case(dsc, orc, 1, 3, 256, 64, 8, 32, False, False, 9931)
 
 
+# Long reductions (Dh up to 2048, 64 K-tiles) at all widths: full oracle checks.
+@pytest.mark.parametrize("B,T,D,Dh,W,H,residual,act", [
+    (2, 300, 512, 256, 8, 8, True, False),
+    (1, 520, 1024, 1024, 4, 16, False, True),  # ragged last tile
+    (1, 200, 512, 2048, 1, 8, True, True),
+    (3, 77, 1024, 2048, 2, 16, True, False),   # sequences inside a tile
+])
+def test_long_reduction(dsc, orc, B, T, D, Dh, W, H, residual, act):
+    run_case(dsc, orc, B, T, D, Dh, W, H, residual, act, 9960 + W + H)
+
+
+def test_many_tiles_sampled(dsc, orc):
+    """B=13, T=2500, D=1024, Dh=1024, W=4, H=16: 508 tiles of 128 tokens x
+    128 columns, more than the CUs; the sequence length is no multiple of the
+    tile."""
+    sampled_case(dsc, orc, 13, 2500, 1024, 1024, 4, 16, True, True, 9970)
+
+
 def test_qkv_shape_sampled(dsc, orc):
     """B=8, T=2048, D=6144, Dh=2048, W=4, H=16 (the Q,K,V projection of a
     2048-wide model); sampled tokens checked through the oracle on their
     causal window (the output at t depends on tokens t-W+1 .. t only)."""
-    B, T, D, Dh, W, H = 8, 2048, 6144, 2048, 4, 16
-    x, xh, M = inputs(B, T, D, Dh, W, H, 9940)
-    y = dsc.headwise_gen_fwd(x.to(gu.dev()), xh.to(gu.dev()), M.to(gu.dev()), W, H, True, False)
+    sampled_case(dsc, orc, 8, 2048, 6144, 2048, 4, 16, True, False, 9940)
+
+
+def test_wide_sampled(dsc, orc):
+    """B=16, T=2048, D=2048, Dh=128, W=4, H=16: 512 filter columns over
+    32768 tokens."""
+    sampled_case(dsc, orc, 16, 2048, 2048, 128, 4, 16, False, True, 9950)
+
+
+def sampled_case(dsc, orc, B, T, D, Dh, W, H, residual, act, seed):
+    gu.say(f"  gen sampled B={B} T={T} D={D} Dh={Dh} W={W} H={H}")
+    x, xh, M = inputs(B, T, D, Dh, W, H, seed)
+    y = dsc.headwise_gen_fwd(x.to(gu.dev()), xh.to(gu.dev()), mt(M), W, H, residual, act)
     torch.cuda.synchronize()
     Mf = gu.f64(M)
     got, ref = [], []
-    for b, t in gu.sample_rows(B, T, 16, 9941):
+    for b, t in gu.sample_rows(B, T, 16, seed + 1):
         s0 = max(0, t - W + 1)
         yo = orc.headwise_gen_fwd(gu.f64(x[b:b + 1, s0:t + 1]), gu.f64(xh[b:b + 1, s0:t + 1]), Mf,
-                                  H, True, False)
+                                  H, residual, act)
         ref.append(yo[0, -1])
         got.append(gu.f64(y[b, t]))
     gu.check("sampled y", np.stack(got), np.stack(ref), torch.bfloat16, "y")
