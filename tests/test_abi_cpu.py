@@ -245,3 +245,21 @@ def test_varlen_checks(lib):
         1, 8, 64, 4, 1, 16, 1, 0, None)
     assert lv(pos=0) == INVALID
     assert lv(pos=A + 4 * BIG + 64) == INVALID               # dx overlaps pos
+
+
+def gfw(lib, x=A, xh=A + BIG, Mt=A + 2 * BIG, y=A + 3 * BIG, B=1, T=8, D=64, Dh=64, W=4, H=8,
+        dt=1, fl=0):
+    p = ctypes.c_void_p
+    return lib.dsc_headwise_gen_fwd(p(x), p(xh), p(Mt), p(y), B, T, D, Dh, W, H, dt, fl, None)
+
+
+def test_generated_filter_checks(lib):
+    assert gfw(lib, dt=0) == UNSUP                           # bf16 only
+    assert gfw(lib, W=3) == UNSUP                            # W in {1, 2, 4, 8}
+    assert gfw(lib, H=4) == UNSUP                            # H a multiple of 8
+    assert gfw(lib, Dh=96) == UNSUP                          # Dh a multiple of 64
+    assert gfw(lib, Dh=0) == UNSUP
+    assert gfw(lib, D=72, H=24, W=1) == UNSUP                # G*W = 3
+    assert gfw(lib, Mt=0) == INVALID
+    assert gfw(lib, y=A + 2 * BIG + 16) == INVALID           # y overlaps Mt
+    assert gfw(lib, B=0, x=0, xh=0, y=0) == 0                # empty: nothing is read
