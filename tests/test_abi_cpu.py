@@ -260,6 +260,7 @@ def test_generated_filter_checks(lib):
     assert gfw(lib, Dh=96) == UNSUP                          # Dh a multiple of 64
     assert gfw(lib, Dh=0) == UNSUP
     assert gfw(lib, D=72, H=24, W=1) == UNSUP                # G*W = 3
+    assert gfw(lib, D=8, H=8, W=4) == UNSUP                  # G*W = 4
     assert gfw(lib, Mt=0) == INVALID
     assert gfw(lib, y=A + 2 * BIG + 16) == INVALID           # y overlaps Mt
     assert gfw(lib, B=0, x=0, xh=0, y=0) == 0                # empty: nothing is read

@@ -55,6 +55,13 @@ def test_channel_blocks_and_ragged(dsc, orc):
     run_case(dsc, orc, 2, 33, 1032, 64, 8, 8, True, False, 9921)
 
 
+def test_narrowest_shapes(dsc, orc):
+    """The fewest filter columns the kernel takes (G*W = 8, one partial
+    column block): D = 16 in two groups at W=4, D = 64 in eight groups at W=1."""
+    run_case(dsc, orc, 1, 50, 16, 64, 4, 8, True, True, 9935)
+    run_case(dsc, orc, 3, 5, 64, 128, 1, 8, False, False, 9936)
+
+
 def test_one_token_sequences_and_short_batches(dsc, orc):
     run_case(dsc, orc, 5, 1, 512, 64, 4, 8, True, True, 9930)
     run_case(dsc, orc, 1, 3, 256, 64, 8, 32, False, False, 9931)
