@@ -399,13 +399,14 @@ def varlen_bench(dsc, di, torch, dev, steps, per_kernel_ms):
     return out
 
 
-def gen_bench(dsc, di, torch, dev, steps, Dh=2048):
-    """Filters generated from a hidden state xh (B, T, Dh) of a 2048-wide model
-    at the step's head-wise shape (H=16, W=4, bf16, residual), forward only:
-    the fused kernel (w = xh M on chip, M passed as Mt (G*W, Dh)) against the
-    unfused pair, a library GEMM writing w (torch.matmul on hipBLASLt, timed
-    with M in both layouts and the faster kept) then the head-wise forward
-    reading it.  Each timing reads its own copies.  Not part of the step."""
+def gen_setup(dsc, di, torch, dev, Dh=2048):
+    """Inputs and launchers of the generated-filter comparison: filters from a
+    hidden state xh (B, T, Dh) of a 2048-wide model at the step's head-wise
+    shape (H=16, W=4, bf16, residual), forward only.  `fused` is the kernel
+    that forms w = xh M on chip (M passed as Mt (G*W, Dh)); the unfused pair
+    is a library GEMM writing w (torch.matmul on hipBLASLt, with M as (Dh, G*W)
+    or as the transposed view of Mt) then the head-wise forward reading it.
+    The fused and unfused launches read separate input copies."""
     B, T, D, W, Hh = (WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"],
                       WORKLOAD["H_headwise"])
     G, N = D // Hh, B * T
@@ -432,9 +433,18 @@ def gen_bench(dsc, di, torch, dev, steps, Dh=2048):
     def gemm_only():
         torch.matmul(xh2.view(N, Dh), M, out=w2.view(N, G * W))
 
+    meta = {"B": B, "T": T, "D": D, "Dh": Dh, "W": W, "H": Hh, "G": G, "N": N}
+    return {"fused": fused, "unfused_M": unfused_nn, "unfused_Mt": unfused_nt,
+            "library_gemm_alone": gemm_only}, meta
+
+
+def gen_bench(dsc, di, torch, dev, steps):
+    """Event-timed comparison of the fused generated-filter forward with the
+    unfused pair (see gen_setup).  Not part of the step."""
+    fns, m = gen_setup(dsc, di, torch, dev)
+    stream = torch.cuda.current_stream()
     out = {}
-    for name, fn in (("fused", fused), ("unfused_M", unfused_nn), ("unfused_Mt", unfused_nt),
-                     ("library_gemm_alone", gemm_only)):
+    for name, fn in fns.items():
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -447,12 +457,88 @@ def gen_bench(dsc, di, torch, dev, steps, Dh=2048):
         torch.cuda.synchronize()
         out[f"{name}_us"] = round(sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3, 1)
     out["unfused_us"] = min(out["unfused_M_us"], out["unfused_Mt_us"])
-    flops = 2.0 * N * Dh * G * W
+    flops = 2.0 * m["N"] * m["Dh"] * m["G"] * m["W"]
     out["gemm_tflops_fused"] = round(flops / (out["fused_us"] * 1e-6) / 1e12, 1)
-    out["hbm_bytes_fused"] = 2 * (N * Dh + Dh * G * W + 2 * N * D)
+    out["hbm_bytes_fused"] = 2 * (m["N"] * m["Dh"] + m["Dh"] * m["G"] * m["W"]
+                                  + 2 * m["N"] * m["D"])
     out["fused_over_unfused"] = round(out["fused_us"] / out["unfused_us"], 3)
-    out["config"] = f"B={B} T={T} D={D} Dh={Dh} W={W} H={Hh}"
+    out["config"] = f"B={m['B']} T={m['T']} D={m['D']} Dh={m['Dh']} W={m['W']} H={m['H']}"
     return out
+
+
+def gen_profile(dsc, di, torch, dev, calls):
+    """Counter passes of the generated-filter comparison: `calls` launches of
+    the fused kernel and of the unfused pair (M transposed), each followed by
+    the 512 MiB device copy that calibrates the counters.  No timing."""
+    fns, _ = gen_setup(dsc, di, torch, dev)
+    src = torch.empty(1 << 28, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(calls):
+        fns["fused"]()
+        fns["unfused_Mt"]()
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+GEN_KERNELS = {"fused (w formed on chip)": "gen_fwd_kernel",
+               "library GEMM writing w": "Cijk_",
+               "head-wise forward reading w": "hw_fwd_kernel"}
+
+
+def summarize_gen_profiles(d, calls):
+    """profiles/generated_filter_traffic.md from the three rocprofv3 runs of
+    `python3 bench.py --generated-filters --profile-ops <calls>` under `d`
+    (trace/, fetch/, write/ as for --summarize-profiles)."""
+    import csv
+    import collections
+
+    def kname(n):
+        for k in list(GEN_KERNELS.values()) + [COPY_KERNEL]:
+            if k in n:
+                return k
+        return None
+
+    stats = {}
+    for row in csv.DictReader(open(os.path.join(d, "trace", "run_kernel_stats.csv"))):
+        k = kname(row["Name"])
+        if k:
+            stats[k] = (int(row["Calls"]), float(row["AverageNs"]) / 1e3)
+
+    def counter(sub, name):
+        per = collections.defaultdict(dict)
+        for row in csv.DictReader(open(os.path.join(d, sub, "run_counter_collection.csv"))):
+            k = kname(row["Kernel_Name"])
+            if k and row["Counter_Name"] == name:
+                di_ = int(row["Dispatch_Id"])
+                per[k][di_] = per[k].get(di_, 0.0) + float(row["Counter_Value"])
+        last = sorted(per[COPY_KERNEL])[-calls:]  # the 512 MiB copies, not the input copies
+        per[COPY_KERNEL] = {i: per[COPY_KERNEL][i] for i in last}
+        return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+    fetch, write = counter("fetch", "FETCH_SIZE"), counter("write", "WRITE_SIZE")
+    ff, wf = COPY_KIB / fetch[COPY_KERNEL], COPY_KIB / write[COPY_KERNEL]
+    cmd = ("rocprofv3 {opt} --output-format csv -d <out>/{sub} -o run -- "
+           f"python3 bench.py --generated-filters --profile-ops {calls}")
+    lines = ["# HBM traffic of the generated-filter comparison, B=8 T=2048 D=6144 Dh=2048 W=4 "
+             "H=16 bf16 (residual)", "",
+             "Commands (repository root, MI355X, TMPDIR=/tmp), then the summary:", ""]
+    for opt, sub in (("--kernel-trace --stats", "trace"), ("--pmc FETCH_SIZE", "fetch"),
+                     ("--pmc WRITE_SIZE", "write")):
+        lines.append("    " + cmd.format(opt=opt, sub=sub))
+    lines += [f"    python3 bench.py --summarize-gen-profiles <out> --profile-ops {calls}", "",
+              f"Calibration: the {COPY_KIB // 1024} MiB device copy reads FETCH_SIZE "
+              f"{fetch[COPY_KERNEL]:.0f} KiB and writes WRITE_SIZE {write[COPY_KERNEL]:.0f} KiB "
+              f"per call, so HBM bytes = {ff:.3f} x FETCH_SIZE + {wf:.3f} x WRITE_SIZE (KiB).",
+              "", "| path | kernel | calls | avg us | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB |",
+              "|---|---|---|---|---|---|---|"]
+    for what, k in GEN_KERNELS.items():
+        n, us = stats.get(k, (0, float("nan")))
+        hb = (ff * fetch.get(k, 0.0) + wf * write.get(k, 0.0)) * 1024
+        lines.append(f"| {what} | `{k}` | {n} | {us:.1f} | {fetch.get(k, 0):.0f} | "
+                     f"{write.get(k, 0):.0f} | {hb / 1e6:.1f} |")
+    with open(os.path.join(ROOT, "profiles", "generated_filter_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def decode_bench(dsc, di, torch, dev, iters=200):
@@ -525,10 +611,17 @@ def main():
     ap.add_argument("--other-configs", action="store_true",
                     help="time the MLP and linear-RNN configurations instead of the step")
     ap.add_argument("--generated-filters", action="store_true",
-                    help="time only the generated-filter comparison (fused against unfused)")
+                    help="time only the generated-filter comparison (fused against unfused); "
+                         "with --profile-ops, run its counter passes instead")
+    ap.add_argument("--summarize-gen-profiles", metavar="DIR",
+                    help="summarise the generated-filter counter runs under DIR into profiles/ "
+                         "(no GPU)")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.profile_ops)
+        return
+    if args.summarize_gen_profiles:
+        summarize_gen_profiles(args.summarize_gen_profiles, args.profile_ops)
         return
     if args.summarize_trace:
         d, name = args.summarize_trace
@@ -552,6 +645,10 @@ def main():
         print(json.dumps({"other_configs": other_configs(dsc, di, torch)}), flush=True)
         return
     if args.generated_filters:
+        if args.profile_ops:
+            gen_profile(dsc, di, torch, dev, args.profile_ops)
+            print("bench: profile passes done", file=sys.stderr, flush=True)
+            return
         print(json.dumps({"generated_filters": gen_bench(dsc, di, torch, dev, args.steps)}),
               flush=True)
         return

@@ -73,6 +73,8 @@ def test_one_token_sequences_and_short_batches(dsc, orc):
     (1, 520, 1024, 1024, 4, 16, False, True),  # ragged last tile
     (1, 200, 512, 2048, 1, 8, True, True),
     (3, 77, 1024, 2048, 2, 16, True, False),   # sequences inside a tile
+    (2, 256, 1024, 256, 4, 16, True, False),   # XCD-grouped order: 4 token tiles x 2 column blocks
+    (4, 1024, 2048, 512, 8, 16, False, True),  # XCD-grouped order over 32 token tiles
 ])
 def test_long_reduction(dsc, orc, B, T, D, Dh, W, H, residual, act):
     run_case(dsc, orc, B, T, D, Dh, W, H, residual, act, 9960 + W + H)
