@@ -406,62 +406,74 @@ def gen_setup(dsc, di, torch, dev, Dh=2048):
     that forms w = xh M on chip (M passed as Mt (G*W, Dh)); the unfused pair
     is a library GEMM writing w (torch.matmul on hipBLASLt, with M as (Dh, G*W)
     or as the transposed view of Mt) then the head-wise forward reading it.
-    The fused and unfused launches read separate input copies."""
+    Each launcher takes a set index: two input sets of x and xh alternate
+    (536 MB, more than the last-level cache holds), so no call finds its
+    inputs cached by the call before."""
     B, T, D, W, Hh = (WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"],
                       WORKLOAD["H_headwise"])
     G, N = D // Hh, B * T
     stream = torch.cuda.current_stream()
     mk = lambda shape, std, seed: di.randn(shape, std, seed, "bf16").to(dev)
-    x1, xh1 = mk((B, T, D), 1.0, 70), mk((B, T, Dh), 1.0, 71)
-    x2, xh2 = mk((B, T, D), 1.0, 72), mk((B, T, Dh), 1.0, 73)
+    sets = [(mk((B, T, D), 1.0, 70 + 2 * i), mk((B, T, Dh), 1.0, 71 + 2 * i)) for i in range(2)]
     M = mk((Dh, G * W), (0.25 / Dh) ** 0.5, 74)
     Mt = M.t().contiguous()
-    y1, y2 = torch.empty_like(x1), torch.empty_like(x2)
+    ys = [torch.empty_like(sets[0][0]) for _ in range(2)]
     w2 = torch.empty((B, T, G, W), dtype=torch.bfloat16, device=dev)
 
-    def fused():
-        dsc.dsc_headwise_gen_fwd(x1, xh1, Mt, y1, W, Hh, True, False, stream)
+    def fused(i):
+        x, xh = sets[i % 2]
+        dsc.dsc_headwise_gen_fwd(x, xh, Mt, ys[i % 2], W, Hh, True, False, stream)
 
-    def unfused_nn():
-        torch.matmul(xh2.view(N, Dh), M, out=w2.view(N, G * W))
-        dsc.dsc_headwise_fwd(x2, w2, y2, Hh, True, False, stream)
+    def unfused_nn(i):
+        x, xh = sets[i % 2]
+        torch.matmul(xh.view(N, Dh), M, out=w2.view(N, G * W))
+        dsc.dsc_headwise_fwd(x, w2, ys[i % 2], Hh, True, False, stream)
 
-    def unfused_nt():
-        torch.matmul(xh2.view(N, Dh), Mt.t(), out=w2.view(N, G * W))
-        dsc.dsc_headwise_fwd(x2, w2, y2, Hh, True, False, stream)
+    def unfused_nt(i):
+        x, xh = sets[i % 2]
+        torch.matmul(xh.view(N, Dh), Mt.t(), out=w2.view(N, G * W))
+        dsc.dsc_headwise_fwd(x, w2, ys[i % 2], Hh, True, False, stream)
 
-    def gemm_only():
-        torch.matmul(xh2.view(N, Dh), M, out=w2.view(N, G * W))
+    def gemm_only(i):
+        torch.matmul(sets[i % 2][1].view(N, Dh), M, out=w2.view(N, G * W))
 
     meta = {"B": B, "T": T, "D": D, "Dh": Dh, "W": W, "H": Hh, "G": G, "N": N}
     return {"fused": fused, "unfused_M": unfused_nn, "unfused_Mt": unfused_nt,
             "library_gemm_alone": gemm_only}, meta
 
 
-def gen_bench(dsc, di, torch, dev, steps):
+def gen_bench(dsc, di, torch, dev, steps, rounds=5):
     """Event-timed comparison of the fused generated-filter forward with the
-    unfused pair (see gen_setup).  Not part of the step."""
+    unfused pair (see gen_setup), not part of the step: `rounds` rounds, each
+    timing `steps` calls of every path in turn; per path the median call."""
     fns, m = gen_setup(dsc, di, torch, dev)
     stream = torch.cuda.current_stream()
-    out = {}
+    times = {name: [] for name in fns}
     for name, fn in fns.items():
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        for a, b in ev:
-            a.record(stream)
-            fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        out[f"{name}_us"] = round(sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3, 1)
+        for i in range(4):
+            fn(i)
+    torch.cuda.synchronize()
+    for _ in range(rounds):
+        for name, fn in fns.items():
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for i, (a, b) in enumerate(ev):
+                a.record(stream)
+                fn(i)
+                b.record(stream)
+            torch.cuda.synchronize()
+            times[name] += [a.elapsed_time(b) * 1e3 for a, b in ev]
+    out = {}
+    for name, t in times.items():
+        t = sorted(t)
+        out[f"{name}_us"] = round(t[len(t) // 2], 1)
     out["unfused_us"] = min(out["unfused_M_us"], out["unfused_Mt_us"])
     flops = 2.0 * m["N"] * m["Dh"] * m["G"] * m["W"]
     out["gemm_tflops_fused"] = round(flops / (out["fused_us"] * 1e-6) / 1e12, 1)
     out["hbm_bytes_fused"] = 2 * (m["N"] * m["Dh"] + m["Dh"] * m["G"] * m["W"]
                                   + 2 * m["N"] * m["D"])
     out["fused_over_unfused"] = round(out["fused_us"] / out["unfused_us"], 3)
+    out["timing"] = f"median of {rounds} x {steps} calls per path, rounds interleaved"
     out["config"] = f"B={m['B']} T={m['T']} D={m['D']} Dh={m['Dh']} W={m['W']} H={m['H']}"
     return out
 
@@ -473,9 +485,9 @@ def gen_profile(dsc, di, torch, dev, calls):
     fns, _ = gen_setup(dsc, di, torch, dev)
     src = torch.empty(1 << 28, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
-    for _ in range(calls):
-        fns["fused"]()
-        fns["unfused_Mt"]()
+    for i in range(calls):
+        fns["fused"](i)
+        fns["unfused_Mt"](i)
         dst.copy_(src)
     torch.cuda.synchronize()
 
