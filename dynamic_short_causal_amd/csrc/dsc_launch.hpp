@@ -51,12 +51,14 @@ struct LrBwdPlan {
 // also fill whole rounds of `resident` concurrent workgroups (MI355X: 256
 // CUs), since a last, partial round leaves CUs idle.  Picks the longest power
 // of two in 64..2048 whose rounds are at least 90 % full, else the fullest.
+// Never below 16 (one tile), also for an empty grid, so that the chunk count
+// (T + tc - 1) / tc is always defined.
 inline int pick_chunk(int64_t B, int64_t T, int64_t ncb, int64_t resident) {
+  if (B <= 0 || T <= 0 || ncb <= 0) return 16;
   int best = 64;
   double best_eff = -1.0;
   for (int tc = 2048; tc >= 64; tc /= 2) {
     const int64_t wg = B * ((T + tc - 1) / tc) * ncb;
-    if (wg <= 0) return (int)((T + 15) / 16 * 16);
     const int64_t rounds = (wg + resident - 1) / resident;
     const double eff = (double)wg / (double)(rounds * resident);
     if (eff >= 0.9) { best = tc; break; }

@@ -3,11 +3,15 @@ exact bits the GPU saw, the tolerance rule, and windowed oracle calls for
 sampled rows at full benchmark sizes.
 
 Tolerances (the GPU against the fp64 oracle on identical input bits):
-  fp32 : max |gpu - oracle| <= 1e-5 * max(1, max|oracle|)
-  bf16 : max |gpu - oracle| / max|oracle| <= 2e-2 for y, dx and 5e-2 for dw, dz, dU
-The fp32 bound is absolute for outputs of magnitude <= 1 and relative above
-(sums over many channels or tokens, such as dw with large H and dU, have
-magnitudes well above 1).
+  fp32, y, dx, dz : max |gpu - oracle| <= 1e-5 (absolute)
+  fp32, dw, dU    : max |gpu - oracle| <= 1e-5 * max(1, max|oracle|)
+  bf16            : max |gpu - oracle| / max|oracle| <= 2e-2 for y, dx and
+                    5e-2 for dw, dz, dU
+y and dx are sums of at most 2W products per element, dz a sum over the
+filter slots of one token.  dw is a sum over the H channels of a group (and,
+for static filters, over every token of every sequence), dU a sum over every
+token: their magnitudes grow with the length of the sum, and fp32 rounding of
+such a sum grows with its magnitude, so their bound scales with it.
 """
 import sys
 
@@ -16,6 +20,7 @@ import torch
 
 TOL_BF16 = {"y": 2e-2, "dx": 2e-2, "dw": 5e-2, "dz": 5e-2, "dU": 5e-2}
 TOL_F32 = 1e-5
+F32_RELATIVE = ("dw", "dU")   # long sums: bound scales with max|oracle| above 1
 
 
 def say(*a):
@@ -46,7 +51,7 @@ def err(gpu, ref):
 def check(name, gpu, ref, dtype, kind):
     a, m = err(gpu, ref)
     if dtype == torch.float32:
-        lim = TOL_F32 * max(1.0, m)
+        lim = TOL_F32 * max(1.0, m) if kind in F32_RELATIVE else TOL_F32
         ok = a <= lim
         msg = f"{name}: max abs err {a:.3e} (limit {lim:.3e}, max|ref| {m:.3e})"
     else:

@@ -151,6 +151,33 @@ def test_workspace_checks(lib):
     assert lrb(lib, dx=A + 8) == INVALID
 
 
+def test_empty_sequence_workspace_and_checks():
+    """T = 0 (and B = 0) through the backward's tiling plan: the workspace query
+    is 0 and a call that then fails a pointer check returns INVALID.  Run in a
+    child process, since a division by zero in the plan would kill it."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes, sys\n"
+        f"sys.path.insert(0, {ROOT!r})\n"
+        "import dynamic_short_causal_amd as d\n"
+        "lib = d.LIB\n"
+        "for (B, T) in ((1, 0), (0, 5), (0, 0), (3, 0)):\n"
+        "    for dt in (0, 1):\n"
+        "        for H in (1, 2):\n"
+        "            n = lib.dsc_lowrank_bwd_workspace_bytes(B, T, 64, 4, H, 16, dt)\n"
+        "            assert n == 0, (B, T, dt, H, n)\n"
+        "p = ctypes.c_void_p\n"
+        "A, BIG = 1 << 20, 1 << 40\n"
+        "# dU is non-empty (R x G*W) even for T = 0: NULL must be rejected\n"
+        "st = lib.dsc_lowrank_bwd(p(A), p(A + BIG), p(A + 2 * BIG), p(A + 3 * BIG), p(A + 4 * BIG),\n"
+        "                         p(A + 5 * BIG), p(0), p(0), 0, 1, 0, 64, 4, 1, 16, 1, 0, None)\n"
+        "assert st == 1, st\n"
+        "print('ok')\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), (r.returncode, r.stderr[-2000:])
+
+
 def hdec(lib, x=A, w=A + BIG, st=A + 2 * BIG, y=A + 3 * BIG, B=2, D=64, W=4, H=1, dt=1, fl=0):
     p = ctypes.c_void_p
     return lib.dsc_headwise_decode(p(x), p(w), p(st), p(y), B, D, W, H, dt, fl, None)

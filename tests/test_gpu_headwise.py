@@ -138,8 +138,23 @@ def _full_size(dsc, orc, wl, nrows, seed_offset=0):
 
 
 def test_full_size_qkv(dsc, orc):
-    """D=6144, T=2048, B=8, W=4, H=16, residual: sampled rows + adjoint identity."""
-    _full_size(dsc, orc, di.WORKLOADS["qkv_headwise"], 48)
+    """D=6144, T=2048, B=8, W=4, H=16, residual: every element of y, dx and dw
+    against the whole-batch fp64 oracle."""
+    wl = di.WORKLOADS["qkv_headwise"]
+    gu.say(f"  full-size {wl.name}: generating inputs")
+    inp = di.make(wl)
+    xd, wd, dyd = (inp[k].to(gu.dev()) for k in ("x", "w", "dy"))
+    y = dsc.headwise_fwd(xd, wd, wl.H, wl.residual, wl.act)
+    dx, dw = dsc.headwise_bwd(xd, wd, dyd, wl.H, wl.residual, wl.act)
+    torch.cuda.synchronize()
+    del xd, wd, dyd
+    gu.say("  kernels done; whole-batch oracle")
+    X, Wt, DY = (gu.f64(inp[k]) for k in ("x", "w", "dy"))
+    dtype = torch.bfloat16
+    gu.check("y", y, orc.headwise_fwd(X, Wt, wl.H, wl.residual, wl.act), dtype, "y")
+    dxo, dwo = orc.headwise_bwd(X, Wt, DY, wl.H, wl.residual, wl.act)
+    gu.check("dx", dx, dxo, dtype, "dx")
+    gu.check("dw", dw, dwo, dtype, "dw")
 
 
 @pytest.mark.parametrize("W", [2, 3, 4, 8])
