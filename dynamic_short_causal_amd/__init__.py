@@ -27,7 +27,11 @@ EXPORTS = ("dsc_version", "dsc_status_string", "dsc_last_error", "dsc_headwise_f
            "dsc_lowrank_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
            "dsc_decode_state", "dsc_static_fwd", "dsc_static_bwd_workspace_bytes",
            "dsc_static_bwd", "dsc_headwise_fwd_varlen", "dsc_headwise_bwd_varlen",
-           "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_headwise_gen_fwd")
+           "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_headwise_gen_fwd",
+           "dsc_lowrank_bwd_noalloc")
+
+# bytes of the library-owned buffer behind dsc_lowrank_bwd_noalloc (include/dsc.h)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class DscError(RuntimeError):
@@ -54,6 +58,8 @@ def _load():
     lib.dsc_lowrank_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.dsc_lowrank_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64,
                                     i64, ci, ci, ci, ci, cu, vp]
+    lib.dsc_lowrank_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, ci, ci,
+                                            ci, ci, cu, vp]
     lib.dsc_headwise_decode.argtypes = [vp, vp, vp, vp, i64, i64, ci, ci, ci, cu, vp]
     lib.dsc_lowrank_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, ci, cu, vp]
     lib.dsc_decode_state.argtypes = [vp, vp, i64, i64, i64, ci, ci, vp]
@@ -74,7 +80,8 @@ def _load():
                  "dsc_lowrank_bwd", "dsc_headwise_decode", "dsc_lowrank_decode",
                  "dsc_decode_state", "dsc_static_fwd", "dsc_static_bwd",
                  "dsc_headwise_fwd_varlen", "dsc_headwise_bwd_varlen",
-                 "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_headwise_gen_fwd"):
+                 "dsc_lowrank_fwd_varlen", "dsc_lowrank_bwd_varlen", "dsc_headwise_gen_fwd",
+                 "dsc_lowrank_bwd_noalloc"):
         getattr(lib, name).restype = ci
     return lib
 
@@ -178,6 +185,21 @@ def dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, workspace, W, H, residual=False, ac
     _check(LIB.dsc_lowrank_bwd(_ptr(x), _ptr(z), _ptr(U), _ptr(dy), _ptr(dx), _ptr(dz),
                                _ptr(dU), _ptr(workspace), nbytes, B, T, D, W, H, R,
                                _dtype(x), _flags(residual, act), _stream(stream)))
+    return dx, dz, dU
+
+
+def dsc_lowrank_bwd_noalloc(x, z, U, dy, dx, dz, dU, W, H, residual=False, act=False,
+                            stream=None):
+    """dsc_lowrank_bwd with the library's own partial-sum buffer (no workspace)."""
+    B, T, D = x.shape
+    R = z.shape[-1]
+    for n, t, s in (("x", x, (B, T, D)), ("z", z, (B, T, R)), ("U", U, (R, (D // H) * W)),
+                    ("dy", dy, (B, T, D)), ("dx", dx, (B, T, D)), ("dz", dz, (B, T, R)),
+                    ("dU", dU, (R, (D // H) * W))):
+        _need(t, n, s, x.dtype)
+    _check(LIB.dsc_lowrank_bwd_noalloc(_ptr(x), _ptr(z), _ptr(U), _ptr(dy), _ptr(dx), _ptr(dz),
+                                       _ptr(dU), B, T, D, W, H, R, _dtype(x),
+                                       _flags(residual, act), _stream(stream)))
     return dx, dz, dU
 
 

@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dsc_launch.hpp"
 #include "decode_launch.hpp"
 #include "static_launch.hpp"
@@ -102,6 +104,39 @@ bool headwise_h_ok(int H, int V) {
 dsc_status hip_status(hipError_t e) {
   if (e == hipSuccess) return ok();
   return fail(DSC_ERR_HIP, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+}
+
+// Partial-sum buffer of dsc_lowrank_bwd_noalloc, owned by the library: every
+// GPU the library runs on holds its own copy (a zero-filled .bss segment of
+// the code object, 128 MiB) until the process ends.  In host code `scratch`
+// names a host-side stand-in, never device memory: kernels get the device
+// address looked up below.
+constexpr size_t kScratchBytes = (size_t)DSC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device ordinal
+
+// Device address of `scratch` on the current device, looked up with that
+// device current on the first call there and kept.
+dsc_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DSC_ERR_HIP, "device ordinal %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr || ((uintptr_t)p % 256) != 0)
+      return fail(DSC_ERR_HIP, "scratch buffer of device %d at %p", dev, p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSC_OK;
 }
 
 }  // namespace
@@ -242,12 +277,15 @@ size_t dsc_lowrank_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int W, i
   return dsc::lr_bwd_plan(B, T, D, W, H, R, dtype == DSC_BF16).bytes;
 }
 
+// lib_ws: the partial sums go to the library-owned buffer (dsc_lowrank_bwd_noalloc)
+// instead of the caller's workspace; its device address is looked up only
+// after every host-side check has passed.
 static dsc_status lowrank_bwd_common(const void *x, const void *z, const void *U,
                                      const int32_t *pos, bool varlen, const void *dy, void *dx,
                                      void *dz, void *dU, void *workspace,
                                      size_t workspace_bytes, int64_t B, int64_t T, int64_t D,
                                      int W, int H, int R, dsc_dtype dtype, unsigned flags,
-                                     void *stream) {
+                                     void *stream, bool lib_ws = false) {
   int V = 0;
   dsc_status st = lowrank_check(B, T, D, W, H, R, dtype, flags, &V);
   if (st != DSC_OK) return st;
@@ -258,14 +296,23 @@ static dsc_status lowrank_bwd_common(const void *x, const void *z, const void *U
                span("U", U, n_U, es, false),     span("dy", dy, n_act, es, false),
                span("dx", dx, n_act, es, true),  span("dz", dz, n_z, es, true),
                span("dU", dU, n_U, es, true),
-               span("workspace", workspace, (int64_t)p.bytes, 1, true),
+               span("workspace", lib_ws ? nullptr : workspace, lib_ws ? 0 : (int64_t)p.bytes, 1,
+                    true),
                span("pos", pos, varlen ? B * T : 0, 4, false)};
-  if (p.bytes > 0 && workspace_bytes < p.bytes)
-    return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed",
-                workspace_bytes, p.bytes);
-  if (p.bytes > 0 && workspace == nullptr)
-    return fail(DSC_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", p.bytes);
+  if (lib_ws) {
+    if (p.bytes > kScratchBytes)
+      return fail(DSC_ERR_WORKSPACE,
+                  "this shape needs %zu bytes of partial sums, above the %zu-byte library buffer",
+                  p.bytes, kScratchBytes);
+  } else {
+    if (p.bytes > 0 && workspace_bytes < p.bytes)
+      return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed",
+                  workspace_bytes, p.bytes);
+    if (p.bytes > 0 && workspace == nullptr)
+      return fail(DSC_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", p.bytes);
+  }
   if ((st = check_ptrs(s, 9)) != DSC_OK) return st;
+  if (lib_ws && p.bytes > 0 && (st = scratch_of_current_device(&workspace)) != DSC_OK) return st;
   dsc::LrArgs a{};
   a.x = x; a.z = z; a.U = U; a.dy = dy; a.dx = dx; a.dz = dz; a.dU = dU; a.ws = workspace;
   a.pos = varlen ? pos : nullptr;
@@ -293,6 +340,14 @@ dsc_status dsc_lowrank_bwd_varlen(const void *x, const void *z, const void *U,
                                   unsigned flags, void *stream) {
   return lowrank_bwd_common(x, z, U, pos, true, dy, dx, dz, dU, workspace, workspace_bytes, B,
                             T, D, W, H, R, dtype, flags, stream);
+}
+
+dsc_status dsc_lowrank_bwd_noalloc(const void *x, const void *z, const void *U, const void *dy,
+                                   void *dx, void *dz, void *dU, int64_t B, int64_t T, int64_t D,
+                                   int W, int H, int R, dsc_dtype dtype, unsigned flags,
+                                   void *stream) {
+  return lowrank_bwd_common(x, z, U, nullptr, false, dy, dx, dz, dU, nullptr, 0, B, T, D, W, H,
+                            R, dtype, flags, stream, true);
 }
 
 static dsc_status decode_common(const void *x, const void *w, const void *z, const void *U,

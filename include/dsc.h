@@ -28,7 +28,8 @@
  *
  * Ownership and execution: the caller owns every buffer (workspace
  * included).  The library never allocates, frees or synchronises, keeps no
- * pointer after a call returns and holds no state between calls.  Work is
+ * pointer after a call returns and holds no state between calls, apart from
+ * the one library-owned buffer of dsc_lowrank_bwd_noalloc (below).  Work is
  * queued on `stream` (a hipStream_t; NULL is the legacy default stream) and
  * runs asynchronously; faults during execution surface at the caller's next
  * synchronisation, as usual in HIP.  Outputs are overwritten, never
@@ -139,6 +140,29 @@ dsc_status dsc_lowrank_bwd(const void *x, const void *z, const void *U,
                            void *workspace, size_t workspace_bytes, int64_t B,
                            int64_t T, int64_t D, int W, int H, int R,
                            dsc_dtype dtype, unsigned flags, void *stream);
+
+/*
+ * Low-rank backward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results, checks and errors are those of dsc_lowrank_bwd (plain
+ * rows, no pos), with no workspace argument: the partial sums go to a
+ * buffer the library owns, DSC_NOALLOC_SCRATCH_BYTES (128 MiB) of device
+ * memory per GPU, held from the first use on that GPU until the process ends.
+ * The call allocates nothing (no hipMalloc or allocating library routine).
+ * A shape whose partial sums need more than that buffer
+ * (dsc_lowrank_bwd_workspace_bytes above DSC_NOALLOC_SCRATCH_BYTES) returns
+ * DSC_ERR_WORKSPACE and queues nothing.  The buffer's content on entry is
+ * never read before it is written.  Every call on one GPU shares that GPU's
+ * buffer: calls that overlap in time on one GPU (on different streams, or
+ * from different host threads) race on it and give undefined results;
+ * serialise them.  The device is the current one (hipGetDevice), which must
+ * be the device of `stream`.
+ */
+#define DSC_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+dsc_status dsc_lowrank_bwd_noalloc(const void *x, const void *z, const void *U,
+                                   const void *dy, void *dx, void *dz, void *dU, int64_t B,
+                                   int64_t T, int64_t D, int W, int H, int R, dsc_dtype dtype,
+                                   unsigned flags, void *stream);
 
 /*
  * One-token (decode) steps.  The pages define the convolution over a whole

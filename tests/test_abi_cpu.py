@@ -291,3 +291,24 @@ def test_generated_filter_checks(lib):
     assert gfw(lib, Mt=0) == INVALID
     assert gfw(lib, y=A + 2 * BIG + 16) == INVALID           # y overlaps Mt
     assert gfw(lib, B=0, x=0, xh=0, y=0) == 0                # empty: nothing is read
+
+
+def test_noalloc_checks(lib):
+    """The allocation-free backward: argument errors as dsc_lowrank_bwd, and a
+    shape needing more partial-sum space than the library buffer is refused
+    on the host (no device is touched)."""
+    import dynamic_short_causal_amd as d
+    p = ctypes.c_void_p
+
+    def call(B=1, T=8, D=64, W=4, H=1, R=16, dt=1, fl=0, x=A, dU=A + 6 * BIG):
+        return lib.dsc_lowrank_bwd_noalloc(p(x), p(A + BIG), p(A + 2 * BIG), p(A + 3 * BIG),
+                                           p(A + 4 * BIG), p(A + 5 * BIG), p(dU), B, T, D, W, H,
+                                           R, dt, fl, None)
+    assert call(R=0) == UNSUP
+    assert call(W=9) == UNSUP
+    assert call(x=0) == INVALID
+    assert call(dU=A + 4 * BIG + 16) == INVALID               # dU overlaps dx
+    B, T, D = 16, 4096, 8192
+    assert lib.dsc_lowrank_bwd_workspace_bytes(B, T, D, 4, 1, 16, 1) > d.NOALLOC_SCRATCH_BYTES
+    assert call(B=B, T=T, D=D) == WS
+    assert b"library buffer" in lib.dsc_last_error()
