@@ -274,7 +274,7 @@ size_t dsc_lowrank_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int W, i
                                        dsc_dtype dtype) {
   int V = 0;
   if (lowrank_check(B, T, D, W, H, R, dtype, 0, &V) != DSC_OK) return 0;
-  return dsc::lr_bwd_plan(B, T, D, W, H, R, dtype == DSC_BF16).bytes;
+  return dsc::lr_bwd_workspace(B, T, D, W, H, R, dtype == DSC_BF16);
 }
 
 // lib_ws: the partial sums go to the library-owned buffer (dsc_lowrank_bwd_noalloc)
@@ -290,29 +290,34 @@ static dsc_status lowrank_bwd_common(const void *x, const void *z, const void *U
   dsc_status st = lowrank_check(B, T, D, W, H, R, dtype, flags, &V);
   if (st != DSC_OK) return st;
   const int es = dtype == DSC_BF16 ? 2 : 4;
+  // the backward addresses 16-row slabs of x, dy and dx through 32-bit buffer
+  // offsets, with 2^31 marking a channel past D
+  if (16 * D * es >= ((int64_t)1 << 31))
+    return fail(DSC_ERR_UNSUPPORTED, "low-rank backward: 16 rows of D=%lld exceed 2^31 bytes",
+                (long long)D);
   const int64_t n_act = B * T * D, n_z = B * T * R, n_U = (int64_t)R * (D / H) * W;
-  const dsc::LrBwdPlan p = dsc::lr_bwd_plan(B, T, D, W, H, R, dtype == DSC_BF16);
+  const size_t need = dsc::lr_bwd_workspace(B, T, D, W, H, R, dtype == DSC_BF16);
   Span s[9] = {span("x", x, n_act, es, false),   span("z", z, n_z, es, false),
                span("U", U, n_U, es, false),     span("dy", dy, n_act, es, false),
                span("dx", dx, n_act, es, true),  span("dz", dz, n_z, es, true),
                span("dU", dU, n_U, es, true),
-               span("workspace", lib_ws ? nullptr : workspace, lib_ws ? 0 : (int64_t)p.bytes, 1,
+               span("workspace", lib_ws ? nullptr : workspace, lib_ws ? 0 : (int64_t)need, 1,
                     true),
                span("pos", pos, varlen ? B * T : 0, 4, false)};
   if (lib_ws) {
-    if (p.bytes > kScratchBytes)
+    if (need > kScratchBytes)
       return fail(DSC_ERR_WORKSPACE,
                   "this shape needs %zu bytes of partial sums, above the %zu-byte library buffer",
-                  p.bytes, kScratchBytes);
+                  need, kScratchBytes);
   } else {
-    if (p.bytes > 0 && workspace_bytes < p.bytes)
+    if (need > 0 && workspace_bytes < need)
       return fail(DSC_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu needed",
-                  workspace_bytes, p.bytes);
-    if (p.bytes > 0 && workspace == nullptr)
-      return fail(DSC_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", p.bytes);
+                  workspace_bytes, need);
+    if (need > 0 && workspace == nullptr)
+      return fail(DSC_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
   }
   if ((st = check_ptrs(s, 9)) != DSC_OK) return st;
-  if (lib_ws && p.bytes > 0 && (st = scratch_of_current_device(&workspace)) != DSC_OK) return st;
+  if (lib_ws && need > 0 && (st = scratch_of_current_device(&workspace)) != DSC_OK) return st;
   dsc::LrArgs a{};
   a.x = x; a.z = z; a.U = U; a.dy = dy; a.dx = dx; a.dz = dz; a.dU = dU; a.ws = workspace;
   a.pos = varlen ? pos : nullptr;

@@ -30,6 +30,14 @@ struct LrArgs {
   void *stream;
 };
 
+// Workgroup shape of the low-rank backward for per-channel bf16 filters without
+// activation (lr_bwd_cl_kernel): waves, 16-channel groups per wave, and the
+// workgroups resident on one CU.
+constexpr int kLrClWaves = 4;
+constexpr int kLrClNG = 2;
+constexpr int kLrClCB = 16 * kLrClNG * kLrClWaves;
+constexpr int kLrClResident = 3;
+
 // Tiling of the low-rank backward and the workspace it implies.  Shared by
 // the workspace query and the launcher so the two always agree.
 struct LrBwdPlan {
@@ -68,22 +76,35 @@ inline int pick_chunk(int64_t B, int64_t T, int64_t ncb, int64_t resident) {
   return best < 16 ? 16 : best;
 }
 
-inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int R,
-                             bool bf16) {
+// The kernel a low-rank backward call runs: per-channel bf16 filters without
+// activation take lr_bwd_cl_kernel, everything else lr_bwd_kernel.
+inline bool lr_bwd_uses_cl(int H, bool bf16, bool act) { return bf16 && H == 1 && !act; }
+
+inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int R, bool bf16,
+                             bool cl) {
   LrBwdPlan p{};
   p.V = bf16 ? 8 : 4;
   p.gpv = p.V / H;
   p.units = 1;  // channel vectors per lane (LrGeo::NU)
-  p.cb = (int64_t)4 /*waves*/ * 4 /*quarters*/ * p.units * p.V;
+  p.cb = cl ? kLrClCB : (int64_t)4 /*waves*/ * 4 /*quarters*/ * p.units * p.V;
   p.ncb = (D + p.cb - 1) / p.cb;
   p.rpad = 16;  // R <= 16: one 16-row MFMA block of ranks
-  p.tc = pick_chunk(B, T, p.ncb, 768);  // 3 resident workgroups per CU
+  p.tc = pick_chunk(B, T, p.ncb, (cl ? kLrClResident : 3) * 256);
   p.nchunk = (T + p.tc - 1) / p.tc;
   const int64_t G = D / H;
   p.dz_part = (size_t)p.ncb * (size_t)(B * T) * (size_t)p.rpad * 4;
   p.dU_part = (size_t)(B * p.nchunk) * (size_t)p.rpad * (size_t)(G * W) * 4;
   p.bytes = p.dz_part + p.dU_part;
   return p;
+}
+
+// Workspace of a low-rank backward call with or without activation (the
+// query takes no flags): the larger need of the kernels the shape can take.
+inline size_t lr_bwd_workspace(int64_t B, int64_t T, int64_t D, int W, int H, int R, bool bf16) {
+  const size_t g = lr_bwd_plan(B, T, D, W, H, R, bf16, false).bytes;
+  if (!lr_bwd_uses_cl(H, bf16, false)) return g;
+  const size_t c = lr_bwd_plan(B, T, D, W, H, R, bf16, true).bytes;
+  return c > g ? c : g;
 }
 
 hipError_t headwise_launch(const HwArgs &a);

@@ -93,24 +93,28 @@ __device__ __forceinline__ void store_floats(float *p, const float (&v)[N]) {
   }
 }
 
-constexpr int kClWaves = 4;
-constexpr int kClNG = 2;                       // 16-channel groups per wave
+constexpr int kClWaves = kLrClWaves;           // waves per workgroup
+constexpr int kClNG = kLrClNG;                 // 16-channel groups per wave
+constexpr int kClPF = 1;                       // steps of x, dy, z loads in flight
 constexpr int kClThreads = 64 * kClWaves;
-constexpr int kClCB = 16 * kClNG * kClWaves;   // 128 channels per workgroup
+constexpr int kClCB = kLrClCB;                 // channels per workgroup
+constexpr int kClVPR = kClCB / 8;              // 16-byte vectors per row of the block
+// every thread moves one vector of x and one of dy per step, or (with twice as
+// many threads as vectors of a 16-row slab) one vector of either
+constexpr bool kClSplit = kClThreads == 32 * kClVPR;
+static_assert(kClSplit || kClThreads == 16 * kClVPR, "one or two slab vectors per thread");
 
 template <int W> struct LrBwdClGeo {
-  static constexpr int XP = kClCB * 2 + 32;    // bf16 rows (x ring, dy slab, dx staging)
+  static constexpr int XP = kClCB * 2 + 32;    // bf16 row pitch (x and dy rings, dx staging)
   static constexpr int ZP = 40;                // z ring row: 16 ranks + 8 bytes
-  static constexpr int DSP = 32 * 4 + 16;      // ds ring row of one channel: 32 tokens fp32
   static constexpr int NHQ = (W + 2) / 4;      // x halo quads
-  static constexpr int NDQ = (W + 6) / 4;      // ds quads for dx
+  static constexpr int NDQ = (W + 6) / 4;      // dy quads for dx
   static constexpr int CHK = W * 64 * 8;       // dw chunks of one wave and group
   static constexpr int o_x = 0;
   static constexpr int o_dy = o_x + 32 * XP;
-  static constexpr int o_dx = o_dy + 16 * XP;
+  static constexpr int o_dx = o_dy + 32 * XP;
   static constexpr int o_z = o_dx + 16 * XP;
-  static constexpr int o_ds = o_z + 32 * ZP;
-  static constexpr int o_chk = o_ds + kClCB * DSP;
+  static constexpr int o_chk = o_z + 32 * ZP;
   static constexpr int o_dz = o_chk + kClWaves * CHK;
   static constexpr int o_pos = o_dz + kClWaves * 64 * 16;  // 32 document positions (VL)
   static constexpr int bytes = o_pos + 32 * 4;
@@ -120,15 +124,16 @@ template <int W> struct LrBwdClGeo {
 // kernel resource-usage report; the register count grows with W).
 template <int W, bool VL>
 constexpr int lr_bwd_cl_min_waves() {
-  // the position masks of packed rows tip the widest case over
-  if constexpr (VL && W == 8) return 1;
+  // the position masks of packed rows tip W = 4 and 8 over
+  if constexpr (W == 8) return 1;
+  if constexpr (VL && W == 4) return 2;
   return W <= 4 ? 3 : 2;
 }
 
 // Packed rows (VL): a 32-entry ring of document positions.  A tap k >= 1 of a
 // token beyond its position is dropped: for dx by zeroing that token's z row
-// in the tap-k A operand (one row per lane), for the SiLU recomputation and
-// dw by a per-lane bit mask over (own token, tap), so dz and dU follow.
+// in the tap-k A operand (one row per lane), for dw by a per-lane bit mask
+// over (own token, tap), so dz and dU follow.
 template <int W, bool VL>
 __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr_bwd_cl_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ z, const bf16 *__restrict__ U,
@@ -136,11 +141,11 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
     float *__restrict__ dzp, float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk,
     int ncb, int64_t N, float rho) {
   using Gc = LrBwdClGeo<W>;
-  constexpr int XP = Gc::XP, ZP = Gc::ZP, DSP = Gc::DSP, NHQ = Gc::NHQ, NDQ = Gc::NDQ, NG = kClNG;
-  constexpr int RP = 16;
+  constexpr int XP = Gc::XP, ZP = Gc::ZP, NHQ = Gc::NHQ, NDQ = Gc::NDQ, NG = kClNG;
+  constexpr int RP = 16, VPR = kClVPR;
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char *xring = smem + Gc::o_x, *dyslab = smem + Gc::o_dy, *dxst = smem + Gc::o_dx,
-                *zring = smem + Gc::o_z, *dsring = smem + Gc::o_ds;
+  unsigned char *xring = smem + Gc::o_x, *dyring = smem + Gc::o_dy, *dxst = smem + Gc::o_dx,
+                *zring = smem + Gc::o_z;
   float *dzbuf = reinterpret_cast<float *>(smem + Gc::o_dz);
   int *pring = reinterpret_cast<int *>(smem + Gc::o_pos);
 
@@ -164,8 +169,11 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
     cok[u] = cb * kClCB + cl0[u] + n < D;
   }
 
-  // coop: each thread moves one 16-byte vector of x and one of dy per step
-  const int cr = tid >> 4, cv = tid & 15;
+  // coop role: vector cv of row cr of a 16-row slab; with kClSplit the first
+  // half of the threads moves x and the second half dy
+  const int cidx = kClSplit ? tid % (16 * VPR) : tid;
+  const bool c_x = !kClSplit || tid < 16 * VPR, c_dy = !kClSplit || tid >= 16 * VPR;
+  const int cr = cidx / VPR, cv = cidx % VPR;
   const int cc = cb * kClCB + cv * 8;
   const uint32_t coff = (cc < D ? (uint32_t)cc * 2 : kOOB) + (uint32_t)(cr * D * 2);
   const bool z_on = tid < 16 * R;
@@ -210,56 +218,85 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
   const int tiles = (t1 - t0 + 15) / 16;
   const int nsteps = tiles + 1;
   __syncthreads();
-  {
+  if (c_x) {  // x of the 16 tokens before the chunk (zero before the sequence)
     const int tb = t0 - 16;
     const brsrc rx = slab(x, tb, tb < 0 ? tb : T, D, D);
     const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, coff, 0, kNT));
     *reinterpret_cast<uint4 *>(xring + ((tb + cr) & 31) * XP + cv * 16) = v;
   }
+  // transposing-read address: rows row .. row+3 (lane quads) of columns col0 ..
   auto tra = [&](const unsigned char *base, int row, int col0) {
     return base + row * XP + (col0 + 4 * (n & 3)) * 2;
   };
 
-  uint4 xn, dyn;
-  bf16 zn;
-  int pn = 0;
-  auto issue = [&](int st) {
+  // loads of step st go to slot st % kClPF, kClPF steps ahead
+  uint4 xn[kClPF], dyn[kClPF];
+  bf16 zn[kClPF];
+  int pn[kClPF];
+  auto issue = [&](int st, int sl) {  // sl: compile-time after unrolling
     const int t = t0 + 16 * st;
     const bool halo = st == tiles;
     if constexpr (VL) {
       const brsrc rp = mk_rsrc(pos + seq + t, (int64_t)(min(T, t + 16) - t) * 4);
-      pn = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, tid < 16 ? (uint32_t)tid * 4 : kOOB, 0, 0);
+      pn[sl] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, tid < 16 ? (uint32_t)tid * 4 : kOOB, 0, 0);
     }
     const brsrc rz = slab(z, t, T, R, R);
-    const brsrc rd = slab(dy, t, T, D, D);
-    const brsrc rx = slab(x, t, T, D, D);
-    zn = (bf16)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
-    dyn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, coff, 0, kNT));
-    if (!halo) xn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, coff, 0, kNT));
+    zn[sl] = (bf16)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
+    if (c_dy) {
+      const brsrc rd = slab(dy, t, T, D, D);
+      dyn[sl] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, coff, 0, kNT));
+    }
+    if (c_x && !halo) {
+      const brsrc rx = slab(x, t, T, D, D);
+      xn[sl] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, coff, 0, kNT));
+    }
   };
-  auto fill = [&](int st) {
+  auto fill = [&](int st, int sl) {
     const int t = t0 + 16 * st;
     const bool halo = st == tiles;
-    if (!halo) *reinterpret_cast<uint4 *>(xring + ((t + cr) & 31) * XP + cv * 16) = xn;
-    *reinterpret_cast<uint4 *>(dyslab + cr * XP + cv * 16) = dyn;
-    if (z_on) reinterpret_cast<bf16 *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn;
-    if (VL && tid < 16) pring[(t + tid) & 31] = pn;
+    const int row = (t + cr) & 31;
+    if (c_x && !halo) *reinterpret_cast<uint4 *>(xring + row * XP + cv * 16) = xn[sl];
+    if (c_dy) *reinterpret_cast<uint4 *>(dyring + row * XP + cv * 16) = dyn[sl];
+    if (z_on) reinterpret_cast<bf16 *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn[sl];
+    if (VL && tid < 16) pring[(t + tid) & 31] = pn[sl];
   };
 
-  // ds = dy, so the residual rho dy folds into the tap-0 filter
+  // The device stores of step st (dx of tile st-1 from the staging rows, dz of
+  // tile st summed by wave 0 in wave order; lane (q, j) holds ranks 4q..4q+3
+  // of token t + j) are issued at the start of step st + 1, after its fill and
+  // before its prefetch.  Stores count in the same counter as loads, so the
+  // fill's wait for its prefetched rows then never waits for stores issued
+  // after those loads.
+  auto flush = [&](int st) {
+    const int t = t0 + 16 * st;
+    if (st > 0 && c_x) {
+      const brsrc rdx = slab(dx, t - 16, t1, D, D);
+      const uint4 v = *reinterpret_cast<const uint4 *>(dxst + cr * XP + cv * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rdx, coff, 0, kNT);
+    }
+    if (st < tiles && wave == 0 && t + n < t1) {
+      f32x4 s4 = *reinterpret_cast<const f32x4 *>(dzbuf + lane * 4);
+#pragma unroll
+      for (int w2 = 1; w2 < kClWaves; ++w2) s4 += *reinterpret_cast<const f32x4 *>(dzbuf + (w2 * 64 + lane) * 4);
+      *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + t + n) * RP + 4 * q) = s4;
+    }
+  };
+  // ds = dy, so the residual rho dy folds into the tap-0 filter; dyp holds the
+  // lane's own four dy values of the step before (the first dy quad of its dx)
   const float rho_tap = rho;
-  issue(0);
-  for (int st = 0; st < nsteps; ++st) {
+  float dyp[NG][4];
+  auto step = [&](int st, int sl) {
     const int t = t0 + 16 * st;
     const bool halo = st == tiles;
-    fill(st);
-    if (st + 1 < nsteps) issue(st + 1);
-    __syncthreads();  // (1)
+    fill(st, sl);
+    if (st > 0) flush(st - 1);
+    if (st + kClPF < nsteps) issue(st + kClPF, sl);
+    __syncthreads();  // (1) rings of this step written; staging and dz tiles of the last read
     constexpr int X0 = 4 * NHQ;
-    float ds[NG][4], dyc[NG][4], xw[NG][4 * NHQ + 4];
+    float dyc[NG][4], xw[NG][4 * NHQ + 4];
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
-      const s16x4 v = tr16(tra(dyslab, 4 * q + (n >> 2), cl0[u]));
+      const s16x4 v = tr16(tra(dyring, (t + 4 * q + (n >> 2)) & 31, cl0[u]));
 #pragma unroll
       for (int e = 0; e < 4; ++e) dyc[u][e] = bf2f(v[e]);
 #pragma unroll
@@ -282,16 +319,9 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
       }
     }
     auto own_off = [&](int e, int k) { return VL && k > 0 && ((mown >> (8 * e + k)) & 1u); };
-#pragma unroll
-    for (int u = 0; u < NG; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ds[u][e] = dyc[u][e];
-#pragma unroll
-    for (int u = 0; u < NG; ++u)
-      *reinterpret_cast<f32x4 *>(dsring + (cl0[u] + n) * DSP + ((t + 4 * q) & 31) * 4) =
-          f32x4{ds[u][0], ds[u][1], ds[u][2], ds[u][3]};
-    __builtin_amdgcn_wave_barrier();
     if (st > 0) {
+      // dx of the previous tile: lane (q, n) forms tokens t-16+4q+e, e < 4, from
+      // ds = dy at t-16+4q .. t-16+4q+4*NDQ-1 (first quad: dyp; the rest from the ring)
       s16x4 az[W];
 #pragma unroll
       for (int k = 0; k < W; ++k) {
@@ -302,12 +332,14 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
       }
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        float dw[4 * NDQ];
+        float dq[4 * NDQ];
 #pragma unroll
-        for (int h = 0; h < NDQ; ++h) {
-          const f32x4 v = *reinterpret_cast<const f32x4 *>(dsring + (cl0[u] + n) * DSP + ((t - 16 + 4 * q + 4 * h) & 31) * 4);
+        for (int e = 0; e < 4; ++e) dq[e] = dyp[u][e];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dw[4 * h + e] = v[e];
+        for (int h = 1; h < NDQ; ++h) {
+          const s16x4 v = tr16(tra(dyring, (t - 16 + 4 * q + 4 * h + (n >> 2)) & 31, cl0[u]));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dq[4 * h + e] = bf2f(v[e]);
         }
         float o[4];
 #pragma unroll
@@ -318,7 +350,7 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
           const f32x4 wk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(az[k], bu[u][k], f32x4{ini, ini, ini, ini}, 0, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            o[e] = fmaf(wk[e], dw[e + k], o[e]);
+            o[e] = fmaf(wk[e], dq[e + k], o[e]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -326,6 +358,10 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
               __builtin_bit_cast(uint16_t, (__bf16)o[e]);
       }
     }
+#pragma unroll
+    for (int u = 0; u < NG; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dyp[u][e] = dyc[u][e];
     if (!halo) {
       const s16x4 azt = tr16(zring + ((t + 4 * q + (n >> 2)) & 31) * ZP + 8 * (n & 3));
       // chunk read by this lane; chunk c is stored at slot c ^ (bit 5 of c ->
@@ -342,7 +378,7 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
           float pr[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            pr[e] = own_off(e, k) ? 0.f : ds[u][e] * xw[u][X0 + e - k];
+            pr[e] = own_off(e, k) ? 0.f : dyc[u][e] * xw[u][X0 + e - k];
           const uint32_t p0 = pack_bf16x2(pr[0], pr[1]);
           const uint32_t p1 = pack_bf16x2(pr[2], pr[3]);
           bdw[k] = __builtin_bit_cast(s16x4, make_uint2(p0, p1));
@@ -360,20 +396,17 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
       }
       *reinterpret_cast<f32x4 *>(dzbuf + (wave * 64 + lane) * 4) = dzacc;
     }
-    __syncthreads();  // (2)
-    if (st > 0) {
-      const brsrc rdx = slab(dx, t - 16, t1, D, D);
-      const uint4 v = *reinterpret_cast<const uint4 *>(dxst + cr * XP + cv * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rdx, coff, 0, kNT);
-    }
-    // dz: wave w sums ranks 4w..4w+3 over the 4 waves' tiles (lane j: token t + j)
-    if (!halo && lane < 16 && t + lane < t1) {
-      f32x4 s4 = *reinterpret_cast<const f32x4 *>(dzbuf + (16 * wave + lane) * 4);
+    __syncthreads();  // (2) staging, dz tiles and ring reads of this step complete
+  };
 #pragma unroll
-      for (int w2 = 1; w2 < kClWaves; ++w2) s4 += *reinterpret_cast<const f32x4 *>(dzbuf + (w2 * 64 + 16 * wave + lane) * 4);
-      *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + t + lane) * RP + 4 * wave) = s4;
-    }
+  for (int p = 0; p < kClPF; ++p)
+    if (p < nsteps) issue(p, p);
+  for (int st = 0; st < nsteps; st += kClPF) {
+#pragma unroll
+    for (int p = 0; p < kClPF; ++p)
+      if (st + p < nsteps) step(st + p, p);
   }
+  flush(nsteps - 1);
   // dU partial of this chunk: lane (q, n) holds ranks 4q..4q+3 of channel c,
   // every tap; a rank row of U has channel c's W taps contiguously
   float *dst = dUp + (int64_t)(b * nchunk + chunk) * RP * GW;

@@ -423,7 +423,9 @@ constexpr int lr_bwd_min_waves() {
   // packed rows' position ring takes the per-channel W = 4 case over
   if constexpr (VL && sizeof(E) == 2 && GPV == 8 && W == 4) return 2;
   if constexpr (sizeof(E) == 2)
-    return GPV == 8 && W == 8 ? 1 : (GPV == 8 && W >= 5) || (GPV == 4 && W == 8) ? 2 : 3;
+    return GPV == 8 && W == 8 ? 1
+           : (GPV == 8 && W >= 5) || (GPV == 4 && W == 8) || (VL && GPV == 4 && W == 7) ? 2
+                                                                                         : 3;
   else return GPV == 4 && W >= 7 ? 2 : 3;
 }
 
@@ -608,13 +610,36 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
     for (int i = 0; i < V; ++i) dyp[u][i] = 0.f;
   const float rho_act = ACT ? rho : 0.f;   // residual through dy (SiLU)
   const float rho_tap = ACT ? 0.f : rho;   // residual folded into the tap-0 filter (ds = dy)
+  // The device stores of step st (dx of tile st-1 from the staging rows; the dz
+  // partial of tile st, summed over the 4 waves in wave order) are issued at
+  // the start of step st + 1, after its fill and before its prefetch.  Stores
+  // count in the same counter as loads, so the fill's wait for its prefetched
+  // rows then never waits for stores issued after those loads.
+  auto flush = [&](int st) {
+    const int t = t0 + 16 * st;
+    if (st > 0) {
+      const brsrc rdx = slab(dx, t - 16, t1);
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const uint4 val = *reinterpret_cast<const uint4 *>(dxstage + (p * RPP + rr) * SP + vv * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, val), rdx, voff[p], 0, kNT);
+      }
+    }
+    if (st < tiles && wave == 0 && t + j < t1) {
+      f32x4 s4 = *reinterpret_cast<const f32x4 *>(dzbuf + lane * 4);
+#pragma unroll
+      for (int w2 = 1; w2 < 4; ++w2) s4 += *reinterpret_cast<const f32x4 *>(dzbuf + (w2 * 64 + lane) * 4);
+      *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + t + j) * RP + 4 * q) = s4;
+    }
+  };
   auto step = [&](int st, int sl) {
     const int t = t0 + 16 * st;
     const bool halo = st == tiles;
     const int tau = t + j;
     fill(st, sl);
+    if (st > 0) flush(st - 1);
     if (st + PF < nsteps) issue(st + PF, sl);
-    __syncthreads();  // (1) rings and slabs of this step written
+    __syncthreads();  // (1) rings and slabs of this step written; staging and dz tiles of the last read
     float dxa[NU][V];
 #pragma unroll
     for (int u = 0; u < NU; ++u)
@@ -790,20 +815,6 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
       }
     }
     __syncthreads();  // (2) dx staging and dz partials complete; ring reads done
-    if (st > 0) {
-      const brsrc rdx = slab(dx, t - 16, t1);
-#pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        const uint4 val = *reinterpret_cast<const uint4 *>(dxstage + (p * RPP + rr) * SP + vv * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, val), rdx, voff[p], 0, kNT);
-      }
-    }
-    if (!halo && wave == 0 && tau < t1) {
-      f32x4 s4 = *reinterpret_cast<const f32x4 *>(dzbuf + lane * 4);
-#pragma unroll
-      for (int w2 = 1; w2 < 4; ++w2) s4 += *reinterpret_cast<const f32x4 *>(dzbuf + (w2 * 64 + lane) * 4);
-      *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + tau) * RP + 4 * q) = s4;
-    }
   };
 #pragma unroll
   for (int p = 0; p < PF; ++p)
@@ -813,6 +824,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
     for (int p = 0; p < PF; ++p)
       if (st + p < nsteps) step(st + p, p);
   }
+  flush(nsteps - 1);
   {
     const int qo = lane >> 4, n = lane & 15;
     float *dst = dUp + (int64_t)(b * nchunk + chunk) * RP * GW;

@@ -36,8 +36,8 @@ template <int W, bool VL>
 static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
   hipStream_t s = (hipStream_t)a.stream;
   const float rho = a.residual ? 1.f : 0.f;
-  const LrBwdPlan p = lr_bwd_plan(a.B, a.T, a.D, a.W, a.H, a.R, a.bf16);
-  if (p.cb != kClCB || a.H != 1 || a.act) return hipErrorInvalidValue;
+  const LrBwdPlan p = lr_bwd_plan(a.B, a.T, a.D, a.W, a.H, a.R, a.bf16, true);
+  if (p.cb != kClCB || !lr_bwd_uses_cl(a.H, a.bf16, a.act)) return hipErrorInvalidValue;
   float *dzp = (float *)a.ws;
   float *dUp = (float *)((char *)a.ws + p.dz_part);
   const int64_t nblocks = a.B * p.nchunk * p.ncb;
@@ -56,12 +56,12 @@ static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
 
 template <typename E, int W, int GPV, bool VL>
 static hipError_t launch_lr_bwd(const LrArgs &a) {
-  if (sizeof(E) == 2 && GPV == 8 && !a.act) {  // H == 1, no SiLU
+  if (lr_bwd_uses_cl(a.H, sizeof(E) == 2, a.act)) {  // bf16, H == 1, no SiLU
     return launch_lr_bwd_cl<W, VL>(a);
   } else {
     hipStream_t s = (hipStream_t)a.stream;
     const float rho = a.residual ? 1.f : 0.f;
-    const LrBwdPlan p = lr_bwd_plan(a.B, a.T, a.D, a.W, a.H, a.R, a.bf16);
+    const LrBwdPlan p = lr_bwd_plan(a.B, a.T, a.D, a.W, a.H, a.R, a.bf16, false);
     const int64_t N = a.B * a.T;
     float *dzp = (float *)a.ws;
     float *dUp = (float *)((char *)a.ws + p.dz_part);

@@ -149,6 +149,10 @@ def test_workspace_checks(lib):
     assert lrb(lib, ws=A + 4 * BIG + 16) == INVALID          # workspace overlaps dx
     assert lrb(lib, R=70) == UNSUP
     assert lrb(lib, dx=A + 8) == INVALID
+    # 16 rows of x must fit the backward's 32-bit slab offsets
+    assert lrb(lib, B=1, T=1, D=1 << 26) == UNSUP            # bf16: 16 * 2^26 * 2 = 2^31
+    assert lrb(lib, B=1, T=1, D=(1 << 25), dt=0) == UNSUP    # fp32: 16 * 2^25 * 4 = 2^31
+    assert lrb(lib, B=0, T=1, D=(1 << 26) - 8) != UNSUP
 
 
 def test_empty_sequence_workspace_and_checks():
