@@ -127,6 +127,24 @@ OP_KERNELS = {  # op -> kernel names (rocprofv3) that one call launches
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"  # the 512 MiB device copy of --profile-ops
 COPY_KIB = 524288
+SUM_KERNEL = "native::reduce_kernel"     # torch's read-only sum of the same 512 MiB
+
+
+def op_spans(trace_csv, kernels, calls):
+    """Mean span of one call of an op launching `kernels` in order, from the
+    per-dispatch timestamps of a --kernel-trace run: first kernel's start to
+    the last kernel's end, over the last `calls` calls (in us)."""
+    import csv
+    rows = [r for r in csv.DictReader(open(trace_csv))
+            if any(k in r["Kernel_Name"] for k in kernels)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    first = [i for i, r in enumerate(rows) if kernels[0] in r["Kernel_Name"]]
+    spans = []
+    for a, i in enumerate(first):
+        j = first[a + 1] if a + 1 < len(first) else len(rows)
+        spans.append((int(rows[j - 1]["End_Timestamp"]) - int(rows[i]["Start_Timestamp"])) / 1e3)
+    spans = spans[-calls:]
+    return sum(spans) / len(spans) if spans else float("nan")
 
 
 def summarize_profiles(d, calls):
@@ -138,7 +156,7 @@ def summarize_profiles(d, calls):
     import collections
 
     def kname(n):
-        for k in sorted({k for ks in OP_KERNELS.values() for k in ks} | {COPY_KERNEL},
+        for k in sorted({k for ks in OP_KERNELS.values() for k in ks} | {COPY_KERNEL, SUM_KERNEL},
                         key=len, reverse=True):
             if k in n:
                 return k
@@ -159,12 +177,15 @@ def summarize_profiles(d, calls):
                 per[k][di_] = per[k].get(di_, 0.0) + float(row["Counter_Value"])
         # the device copy kernel also serves the input copies made before the
         # passes: calibrate on its last `calls` dispatches, the 512 MiB copies
-        last = sorted(per[COPY_KERNEL])[-calls:]
-        per[COPY_KERNEL] = {i: per[COPY_KERNEL][i] for i in last}
+        for ck in (COPY_KERNEL, SUM_KERNEL):
+            if ck in per:
+                last = sorted(per[ck])[-calls:]
+                per[ck] = {i: per[ck][i] for i in last}
         return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
     fetch, write = counter("fetch", "FETCH_SIZE"), counter("write", "WRITE_SIZE")
     ff, wf = COPY_KIB / fetch[COPY_KERNEL], COPY_KIB / write[COPY_KERNEL]
+    ff_sum = COPY_KIB / fetch[SUM_KERNEL] if fetch.get(SUM_KERNEL) else float("nan")
     B, T, D, W = WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"], WORKLOAD["W"]
     alg = algorithmic_bytes(B, T, D, W, WORKLOAD["H_headwise"], WORKLOAD["R"],
                             WORKLOAD["H_lowrank"])
@@ -179,7 +200,12 @@ def summarize_profiles(d, calls):
               f"Calibration: the {COPY_KIB // 1024} MiB device copy ({COPY_KERNEL}) reads "
               f"FETCH_SIZE {fetch[COPY_KERNEL]:.0f} KiB and writes WRITE_SIZE "
               f"{write[COPY_KERNEL]:.0f} KiB per call, so HBM bytes = {ff:.3f} x FETCH_SIZE "
-              f"+ {wf:.3f} x WRITE_SIZE (KiB).", "",
+              f"+ {wf:.3f} x WRITE_SIZE (KiB).  Cross-check: a read-only sum of the same "
+              f"{COPY_KIB // 1024} MiB ({SUM_KERNEL}) reads FETCH_SIZE "
+              f"{fetch.get(SUM_KERNEL, float('nan')):.0f} KiB, a factor of {ff_sum:.3f}.", "",
+              "Op span: one call's first kernel start to last kernel end, from the per-dispatch "
+              "timestamps of the trace run (it includes the gap between the kernels of a "
+              "two-kernel op); the benchmark's event times measure this span.", "",
               "| op | kernel | calls | avg us | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB |",
               "|---|---|---|---|---|---|---|"]
     for op, ks in OP_KERNELS.items():
@@ -192,11 +218,16 @@ def summarize_profiles(d, calls):
             lines.append(f"| {op} | {k} | {n} | {us:.1f} | {fetch.get(k, 0):.0f} | "
                          f"{write.get(k, 0):.0f} | {hb / 1e6:.1f} |")
         op_us = sum(stats.get(k, (0, 0.0))[1] for k in ks)
-        lines.append(f"| {op} | (op total) | | {op_us:.1f} | | | {tot / 1e6:.1f} "
+        span = op_spans(os.path.join(d, "trace", "run_kernel_trace.csv"), ks, calls)
+        lines.append(f"| {op} | (sum of kernels) | | {op_us:.1f} | | | {tot / 1e6:.1f} "
                      f"(algorithmic {alg[op] / 1e6:.1f}) |")
+        lines.append(f"| {op} | (op span) | | {span:.1f} | | | algorithmic "
+                     f"{alg[op] / (span * 1e-6) / 1e9:.0f} GB/s = "
+                     f"{alg[op] / (span * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of peak |")
         with open(os.path.join(ROOT, "profiles", f"{op}_qkv_traffic.json"), "w") as f:
             json.dump({"op": op, "kernels": ks, "hbm_bytes_per_launch": round(tot),
                        "algorithmic_bytes": alg[op], "avg_us": round(op_us, 2),
+                       "span_us": round(span, 2),
                        "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
                        "src_digest": src_digest(KERNEL_SOURCES[op])}, f, indent=1)
             f.write("\n")
@@ -220,6 +251,77 @@ def summarize_trace(d, name, title, command):
         nm = nm.split("(")[0]
         lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e3:.1f} |")
+    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# SQ counter passes (at most 8 SQ counters per pass) and the runs they profile
+SQ_PASSES = [
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_LDS SQ_WAIT_INST_LDS",
+    "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES "
+    "SQ_ACTIVE_INST_VALU SQ_WAIT_ANY",
+]
+COUNTER_RUNS = {
+    # name: (title, command profiled)
+    "qkv_counters": ("SQ counters of the step's kernels, B=8 T=2048 D=6144 W=4 bf16 (head-wise "
+                     "H=16, low-rank R=16 H=1, residual)", "python3 bench.py --profile-ops 2"),
+    "mlp_rnn_counters": ("SQ counters of the MLP (head-wise H=64, B=4 T=4096 D=8192, W in "
+                         "2,3,4,8) and linear-RNN (low-rank R=16 H=8 SiLU, B=16 T=4096 D=4608) "
+                         "configurations", "python3 bench.py --other-configs"),
+}
+
+
+def summarize_counters(name, dirs):
+    """profiles/<name>.md from the rocprofv3 --pmc runs in `dirs` (one per
+    pass of SQ_PASSES, each with run_counter_collection.csv): per kernel
+    instance, the mean of each counter per dispatch and unit-free ratios."""
+    import csv
+    import collections
+    title, command = COUNTER_RUNS[name]
+    per = collections.defaultdict(lambda: collections.defaultdict(dict))
+    regs = {}
+    for d in dirs:
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            nm = r["Kernel_Name"]
+            if "dsc::" not in nm:
+                continue
+            nm = nm[len("void "):] if nm.startswith("void ") else nm
+            nm = nm.split("(")[0].replace("dsc::", "").replace("unsigned short", "bf16")
+            di_ = int(r["Dispatch_Id"])
+            per[nm][r["Counter_Name"]][di_] = (per[nm][r["Counter_Name"]].get(di_, 0.0)
+                                               + float(r["Counter_Value"]))
+            regs[nm] = (r["VGPR_Count"], r["Accum_VGPR_Count"], r["LDS_Block_Size"])
+    cols = [c for p_ in SQ_PASSES for c in p_.split()]
+    lines = [f"# {title}", "", "Commands (repository root, MI355X, TMPDIR=/tmp), then the summary:",
+             ""]
+    for i, p_ in enumerate(SQ_PASSES):
+        lines.append(f"    rocprofv3 --pmc {p_} --output-format csv -d <out>/pmc{i} -o run -- "
+                     f"{command}")
+    lines += [f"    python3 bench.py --summarize-counters {name} "
+              + " ".join(f"<out>/pmc{i}" for i in range(len(SQ_PASSES))), "",
+              "Means per dispatch, summed over the device as rocprofv3 reports them.  Ratios: "
+              "VALU/wave and LDS/wave are instructions per wave (VALU includes MFMA); "
+              "lds_wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES and any_wait = SQ_WAIT_ANY / "
+              "SQ_WAVE_CYCLES (share of wave time waiting); conflict = SQ_LDS_BANK_CONFLICT / "
+              "SQ_ACTIVE_INST_LDS.", ""]
+    lines.append("| kernel | " + " | ".join(cols) + " |")
+    lines.append("|---|" + "---|" * len(cols))
+    mean = lambda d_: sum(d_.values()) / len(d_) if d_ else float("nan")
+    for nm in sorted(per):
+        m = {c: mean(per[nm].get(c, {})) for c in cols}
+        lines.append(f"| `{nm}` | " + " | ".join(f"{m[c]:.4g}" for c in cols) + " |")
+    lines += ["", "| kernel | VGPR, AGPR, LDS bytes (from the trace) | VALU/wave | MFMA/wave | "
+                  "LDS/wave | lds_wait | any_wait | conflict |", "|---|---|---|---|---|---|---|---|"]
+    for nm in sorted(per):
+        m = {c: mean(per[nm].get(c, {})) for c in cols}
+        w = m["SQ_WAVES"] or float("nan")
+        wc = m["SQ_WAVE_CYCLES"] or float("nan")
+        al = m["SQ_ACTIVE_INST_LDS"] or float("nan")
+        lines.append(f"| `{nm}` | {', '.join(regs[nm])} | {m['SQ_INSTS_VALU'] / w:.0f} | "
+                     f"{m['SQ_INSTS_MFMA'] / w:.0f} | {m['SQ_INSTS_LDS'] / w:.0f} | "
+                     f"{m['SQ_WAIT_INST_LDS'] / wc:.3f} | {m['SQ_WAIT_ANY'] / wc:.3f} | "
+                     f"{m['SQ_LDS_BANK_CONFLICT'] / al:.3f} |")
     with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -553,6 +655,76 @@ def summarize_gen_profiles(d, calls):
     print("\n".join(lines))
 
 
+# Read/write mixes of the step's ops, as (input shifts, output shifts): a
+# tensor of shift s has 1/2^s the vectors of x (the head-wise filters w and dw
+# are a quarter of x at H=16, W=4).
+CEILING_MIXES = {
+    "read_only": ([0], []),
+    "copy (low-rank fwd)": ([0], [0]),
+    "head-wise fwd (x, w -> y)": ([0, 2], [0]),
+    "2 reads, 1 write (low-rank bwd)": ([0, 0], [0]),
+    "head-wise bwd (x, w, dy -> dx, dw)": ([0, 2, 0], [0, 2]),
+}
+
+
+def stream_ceilings(torch, dev, reps=8):
+    """Best HBM rate of a plain streaming kernel (libdsc_stream.so) for each
+    read/write mix of the step's ops, at the step's tensor sizes (x: B*T*D
+    bf16), over a sweep of grid and block sizes; two tensor sets alternate
+    (more than the last-level cache), median of `reps` launches per shape."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "dynamic_short_causal_amd", "libdsc_stream.so"))
+    lib.dsc_stream_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_uint, ctypes.c_void_p]
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    B, T, D = WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"]
+    n = B * T * D * 2 // 16
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    out = {}
+    for name, (ish, osh) in CEILING_MIXES.items():
+        sets = []
+        for _ in range(2):
+            ins = [torch.empty((n >> s) * 16, dtype=torch.uint8, device=dev) for s in ish]
+            outs = [torch.empty((n >> s) * 16, dtype=torch.uint8, device=dev) for s in osh]
+            for t in ins:
+                t.fill_(1)  # xor of the loads: 0x01010101 or 0, never the sink key
+            ip = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in ins])
+            op = (ctypes.c_void_p * 2)(*[t.data_ptr() for t in outs])
+            sets.append((ins, outs, ip, op))
+        ish_c = (ctypes.c_int * 3)(*ish)
+        osh_c = (ctypes.c_int * 2)(*osh)
+        nbytes = sum(16 * (n >> s) for s in ish + osh)
+        best = (0.0, None)
+        for block in (256, 512, 1024):
+            for grid in (256, 512, 1024, 2048, 4096, 8192):
+                def call(i):
+                    _, _, ip, op = sets[i % 2]
+                    r = lib.dsc_stream_mix(ip, ish_c, len(ish), op, osh_c, len(osh), n, grid,
+                                           block, ctypes.c_void_p(sink.data_ptr()), 0xA5A5A5A5,
+                                           sp)
+                    assert r == 0, r
+                for i in range(2):
+                    call(i)
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(reps)]
+                for i, (a, b) in enumerate(ev):
+                    a.record(stream)
+                    call(i)
+                    b.record(stream)
+                torch.cuda.synchronize()
+                ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+                gbps = nbytes / (ms * 1e-3) / 1e9
+                if gbps > best[0]:
+                    best = (gbps, (grid, block))
+        out[name] = {"gbps": round(best[0], 1), "frac_of_peak": round(best[0] / HBM_PEAK_GBPS, 4),
+                     "bytes": nbytes, "grid": best[1][0], "block": best[1][1]}
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_bench(dsc, di, torch, dev, iters=200):
     """One-token steps at serving batches, for head-wise H=16 and low-rank R=16
     H=1 at D=6144, W=4, bf16, residual.  Two timings of `iters` steps in a row:
@@ -625,6 +797,11 @@ def main():
     ap.add_argument("--generated-filters", action="store_true",
                     help="time only the generated-filter comparison (fused against unfused); "
                          "with --profile-ops, run its counter passes instead")
+    ap.add_argument("--summarize-counters", nargs="+", metavar=("NAME", "DIR"),
+                    help="SQ counter passes under DIR... into profiles/NAME.md; NAME is one of "
+                         + ", ".join(COUNTER_RUNS))
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the streaming ceilings of the step's read/write mixes")
     ap.add_argument("--summarize-gen-profiles", metavar="DIR",
                     help="summarise the generated-filter counter runs under DIR into profiles/ "
                          "(no GPU)")
@@ -634,6 +811,9 @@ def main():
         return
     if args.summarize_gen_profiles:
         summarize_gen_profiles(args.summarize_gen_profiles, args.profile_ops)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1:])
         return
     if args.summarize_trace:
         d, name = args.summarize_trace
@@ -655,6 +835,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.other_configs:
         print(json.dumps({"other_configs": other_configs(dsc, di, torch)}), flush=True)
+        return
+    if args.ceilings:
+        print(json.dumps({"stream_ceilings": stream_ceilings(torch, dev)}), flush=True)
         return
     if args.generated_filters:
         if args.profile_ops:
@@ -710,11 +893,14 @@ def main():
     if args.profile_ops:
         # counter runs: the 512 MiB copy (read and write of known size) calibrates
         # FETCH_SIZE / WRITE_SIZE against the bytes actually moved
-        src = torch.empty(1 << 28, dtype=torch.bfloat16, device=dev)
+        # and a read-only sum of the same 512 MiB cross-checks FETCH_SIZE
+        src = torch.ones(1 << 28, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
+        tot = torch.empty((), dtype=torch.float32, device=dev)
         for _ in range(args.profile_ops):
             step()
             dst.copy_(src)
+            torch.sum(src, dim=0, dtype=torch.float32, out=tot)
         torch.cuda.synchronize()
         print("bench: profile passes done", file=sys.stderr, flush=True)
         return
@@ -759,6 +945,8 @@ def main():
     varlen = varlen_bench(dsc, di, torch, dev, args.steps, per_kernel_ms)
     print("bench: timing generated filters", file=sys.stderr, flush=True)
     gen = gen_bench(dsc, di, torch, dev, args.steps)
+    print("bench: streaming ceilings", file=sys.stderr, flush=True)
+    ceilings = stream_ceilings(torch, dev)
 
     nbytes = algorithmic_bytes(B, T, D, W, Hh, R, Hl)
     ms_per_step = elapsed / args.steps * 1e3
@@ -805,6 +993,7 @@ def main():
         "static_comparator": static,
         "packed_rows": varlen,
         "generated_filters": gen,
+        "stream_ceilings": ceilings,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -88,7 +88,25 @@ def build(jobs=None):
                    check=True)
     os.replace(tmp, LIB)
     build_c_consumer()
+    build_stream_ceiling()
     return LIB
+
+
+STREAM_SRC = os.path.join(CSRC, "stream_ceiling.hip")
+STREAM_LIB = os.path.join(PKG, "libdsc_stream.so")
+
+
+def build_stream_ceiling():
+    """libdsc_stream.so: the streaming kernel the benchmark's ceiling mode
+    measures read/write mixes with (not part of libdsc.so)."""
+    tmp = STREAM_LIB + ".tmp"
+    cmd = [HIPCC, *[f for f in FLAGS if not f.startswith("-Rpass")], "-shared", STREAM_SRC,
+           "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for stream_ceiling.hip:\n{r.stderr}")
+    os.replace(tmp, STREAM_LIB)
+    return STREAM_LIB
 
 
 CONSUMER_SRC = os.path.join(PKG, "examples", "c_consumer.c")
