@@ -228,7 +228,7 @@ static dsc_status lowrank_check(int64_t B, int64_t T, int64_t D, int W, int H, i
   if (st != DSC_OK) return st;
   if (*V % H)
     return fail(DSC_ERR_UNSUPPORTED, "H=%d: low-rank needs H to divide %d", H, *V);
-  if (R < 1 || R > 16) return fail(DSC_ERR_UNSUPPORTED, "R=%d outside 1..16", R);
+  if (R < 1 || R > 64) return fail(DSC_ERR_UNSUPPORTED, "R=%d outside 1..64", R);
   return DSC_OK;
 }
 

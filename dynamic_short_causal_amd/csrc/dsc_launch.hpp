@@ -48,7 +48,7 @@ struct LrBwdPlan {
   int64_t ncb;      // channel blocks
   int tc;           // tokens per workgroup chunk (multiple of 16)
   int64_t nchunk;   // chunks per sequence
-  int64_t rpad;     // R padded to one 16-row MFMA block
+  int64_t rpad;     // R padded to whole 16-row MFMA blocks
   size_t dz_part;   // bytes of dz partials: ncb * B*T * rpad * 4
   size_t dU_part;   // bytes of dU partials: B*nchunk * rpad * G*W * 4
   size_t bytes;     // total workspace
@@ -76,9 +76,15 @@ inline int pick_chunk(int64_t B, int64_t T, int64_t ncb, int64_t resident) {
   return best < 16 ? 16 : best;
 }
 
-// The kernel a low-rank backward call runs: per-channel bf16 filters without
-// activation take lr_bwd_cl_kernel, everything else lr_bwd_kernel.
-inline bool lr_bwd_uses_cl(int H, bool bf16, bool act) { return bf16 && H == 1 && !act; }
+// Blocks of 16 ranks the low-rank kernels are built for: 1, 2 or 4.
+inline int lr_rank_blocks(int R) { return R <= 16 ? 1 : R <= 32 ? 2 : 4; }
+
+// The kernel a low-rank backward call runs: per-channel bf16 filters of at
+// most 16 ranks without activation take lr_bwd_cl_kernel, everything else
+// lr_bwd_kernel.
+inline bool lr_bwd_uses_cl(int H, int R, bool bf16, bool act) {
+  return bf16 && H == 1 && R <= 16 && !act;
+}
 
 inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int R, bool bf16,
                              bool cl) {
@@ -88,7 +94,7 @@ inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int 
   p.units = 1;  // channel vectors per lane (LrGeo::NU)
   p.cb = cl ? kLrClCB : (int64_t)4 /*waves*/ * 4 /*quarters*/ * p.units * p.V;
   p.ncb = (D + p.cb - 1) / p.cb;
-  p.rpad = 16;  // R <= 16: one 16-row MFMA block of ranks
+  p.rpad = 16 * lr_rank_blocks(R);  // whole 16-row MFMA blocks of ranks
   p.tc = pick_chunk(B, T, p.ncb, (cl ? kLrClResident : 3) * 256);
   p.nchunk = (T + p.tc - 1) / p.tc;
   const int64_t G = D / H;
@@ -102,7 +108,7 @@ inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int 
 // query takes no flags): the larger need of the kernels the shape can take.
 inline size_t lr_bwd_workspace(int64_t B, int64_t T, int64_t D, int W, int H, int R, bool bf16) {
   const size_t g = lr_bwd_plan(B, T, D, W, H, R, bf16, false).bytes;
-  if (!lr_bwd_uses_cl(H, bf16, false)) return g;
+  if (!lr_bwd_uses_cl(H, R, bf16, false)) return g;
   const size_t c = lr_bwd_plan(B, T, D, W, H, R, bf16, true).bytes;
   return c > g ? c : g;
 }

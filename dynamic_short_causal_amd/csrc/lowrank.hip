@@ -1,19 +1,33 @@
 // lowrank.hip -- entry of the low-rank launchers (see lowrank_impl.hpp for the
-// kernels and lowrank_launch.hpp for the tiling and dispatch).
+// kernels and lowrank_launch.hpp for the tiling and dispatch): picks the
+// instance set for the dtype, direction, packed rows and rank blocks.
 #include "dsc_device.hpp"
 #include "dsc_launch.hpp"
 
 namespace dsc {
 
-template <typename E, bool BWD, bool VL> hipError_t lr_dispatch(const LrArgs &a);
-extern template hipError_t lr_dispatch<bf16, false, false>(const LrArgs &a);
-extern template hipError_t lr_dispatch<bf16, true, false>(const LrArgs &a);
-extern template hipError_t lr_dispatch<float, false, false>(const LrArgs &a);
-extern template hipError_t lr_dispatch<float, true, false>(const LrArgs &a);
-extern template hipError_t lr_dispatch<bf16, false, true>(const LrArgs &a);
-extern template hipError_t lr_dispatch<bf16, true, true>(const LrArgs &a);
-extern template hipError_t lr_dispatch<float, false, true>(const LrArgs &a);
-extern template hipError_t lr_dispatch<float, true, true>(const LrArgs &a);
+template <typename E, int RB, bool BWD, bool VL> hipError_t lr_dispatch_rb(const LrArgs &a);
+#define DSC_LR_EXTERN(E, RB)                                                   \
+  extern template hipError_t lr_dispatch_rb<E, RB, false, false>(const LrArgs &a); \
+  extern template hipError_t lr_dispatch_rb<E, RB, true, false>(const LrArgs &a);  \
+  extern template hipError_t lr_dispatch_rb<E, RB, false, true>(const LrArgs &a);  \
+  extern template hipError_t lr_dispatch_rb<E, RB, true, true>(const LrArgs &a);
+DSC_LR_EXTERN(bf16, 1)
+DSC_LR_EXTERN(bf16, 2)
+DSC_LR_EXTERN(bf16, 4)
+DSC_LR_EXTERN(float, 1)
+DSC_LR_EXTERN(float, 2)
+DSC_LR_EXTERN(float, 4)
+#undef DSC_LR_EXTERN
+
+template <typename E, bool BWD, bool VL>
+static hipError_t lr_dispatch(const LrArgs &a) {
+  switch (lr_rank_blocks(a.R)) {
+    case 1: return lr_dispatch_rb<E, 1, BWD, VL>(a);
+    case 2: return lr_dispatch_rb<E, 2, BWD, VL>(a);
+    default: return lr_dispatch_rb<E, 4, BWD, VL>(a);
+  }
+}
 
 template <bool VL>
 static hipError_t lowrank_vl(const LrArgs &a) {

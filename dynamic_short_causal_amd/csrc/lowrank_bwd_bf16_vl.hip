@@ -1,7 +1,7 @@
-// lowrank_bwd_bf16_vl.hip -- instantiates the low-rank bwd launchers for bf16
-// on rows packed with documents (per-token positions).
+// lowrank_bwd_bf16_vl.hip -- instantiates the low-rank bwd launchers for bf16 (packed rows) with
+// DSC_LR_RB blocks of 16 ranks; the build compiles it once per block count.
 #include "lowrank_launch.hpp"
 
 namespace dsc {
-template hipError_t lr_dispatch<bf16, true, true>(const LrArgs &a);
+template hipError_t lr_dispatch_rb<bf16, DSC_LR_RB, true, true>(const LrArgs &a);
 }  // namespace dsc

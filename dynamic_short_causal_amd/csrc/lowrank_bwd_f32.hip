@@ -1,6 +1,7 @@
-// lowrank_bwd_f32.hip -- instantiates the low-rank bwd launchers for f32 (plain rows).
+// lowrank_bwd_f32.hip -- instantiates the low-rank bwd launchers for float (plain rows) with
+// DSC_LR_RB blocks of 16 ranks; the build compiles it once per block count.
 #include "lowrank_launch.hpp"
 
 namespace dsc {
-template hipError_t lr_dispatch<float, true, false>(const LrArgs &a);
+template hipError_t lr_dispatch_rb<float, DSC_LR_RB, true, false>(const LrArgs &a);
 }  // namespace dsc

@@ -1,6 +1,7 @@
-// lowrank_fwd_bf16.hip -- instantiates the low-rank fwd launchers for bf16 (plain rows).
+// lowrank_fwd_bf16.hip -- instantiates the low-rank fwd launchers for bf16 (plain rows) with
+// DSC_LR_RB blocks of 16 ranks; the build compiles it once per block count.
 #include "lowrank_launch.hpp"
 
 namespace dsc {
-template hipError_t lr_dispatch<bf16, false, false>(const LrArgs &a);
+template hipError_t lr_dispatch_rb<bf16, DSC_LR_RB, false, false>(const LrArgs &a);
 }  // namespace dsc

@@ -1,7 +1,7 @@
-// lowrank_fwd_f32_vl.hip -- instantiates the low-rank fwd launchers for f32
-// on rows packed with documents (per-token positions).
+// lowrank_fwd_f32_vl.hip -- instantiates the low-rank fwd launchers for float (packed rows) with
+// DSC_LR_RB blocks of 16 ranks; the build compiles it once per block count.
 #include "lowrank_launch.hpp"
 
 namespace dsc {
-template hipError_t lr_dispatch<float, false, true>(const LrArgs &a);
+template hipError_t lr_dispatch_rb<float, DSC_LR_RB, false, true>(const LrArgs &a);
 }  // namespace dsc

@@ -54,7 +54,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLrThreads = 256;
 
-template <typename E, int W, int GPV> struct LrGeo {
+// RB: blocks of 16 ranks (R <= 16 * RB)
+template <typename E, int W, int GPV, int RB = 1> struct LrGeo {
   static constexpr bool BF = sizeof(E) == 2;
   static constexpr int V = Vw<E>::n;
   static constexpr int H = V / GPV;         // channels per filter group
@@ -66,7 +67,7 @@ template <typename E, int W, int GPV> struct LrGeo {
   static constexpr int NS = NG * W;         // filter slots per lane
   static constexpr int CW = 4 * NU * V;     // channels per wave
   static constexpr int CB = 4 * CW;         // channels per workgroup
-  static constexpr int KS = BF ? 1 : 4;     // rank steps per filter MFMA (R <= 16)
+  static constexpr int KS = BF ? RB : 4 * RB;  // filter MFMAs per output: 16 (bf16) or 4 ranks each
   // LDS rings (per wave): 32 token rows of x (raw) and of ds (fp32), each row
   // padded by 16 bytes so that 16 consecutive rows spread over the banks
   static constexpr int XROW = CW * (int)sizeof(E) + 16;
@@ -111,11 +112,11 @@ __device__ __forceinline__ int slot_col(int cw, int qq, int k, int m, int D) {
 // A operands of the filter MFMAs: for tap k, part p, rank step ks, lane (qa, i)
 // holds U[ranks of K-quarter qa][column of output row i]; row i = 4*qo + e of
 // the output goes to lane quarter qo as slot m = 4p + e of tap k.
-template <typename E, int W, int GPV>
+template <typename E, int W, int GPV, int RB>
 __device__ __forceinline__ void load_wA(
     const E *__restrict__ U, int GW, int R, int cw, int D, int lane,
-    typename WFrag<sizeof(E) == 2>::T (&a)[W][LrGeo<E, W, GPV>::NP][LrGeo<E, W, GPV>::KS]) {
-  using Gm = LrGeo<E, W, GPV>;
+    typename WFrag<sizeof(E) == 2>::T (&a)[W][LrGeo<E, W, GPV, RB>::NP][LrGeo<E, W, GPV, RB>::KS]) {
+  using Gm = LrGeo<E, W, GPV, RB>;
   const int qa = lane >> 4, i = lane & 15, qo = i >> 2, e = i & 3;
 #pragma unroll
   for (int k = 0; k < W; ++k)
@@ -129,7 +130,7 @@ __device__ __forceinline__ void load_wA(
           s16x4 f;
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
-            const int r = 4 * qa + e2;
+            const int r = 16 * ks + 4 * qa + e2;
             f[e2] = (col >= 0 && r < R) ? (short)U[(int64_t)r * GW + col] : (short)0;
           }
           a[k][p][ks] = f;
@@ -154,7 +155,7 @@ __device__ __forceinline__ void load_zB(const E *__restrict__ z, int64_t tok, bo
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if constexpr (BF) {
-      const int r0 = 4 * q;
+      const int r0 = 16 * ks + 4 * q;
       s16x4 f;
       if ((R & 3) == 0) {  // 8-byte aligned 4-rank groups, all in or all out
         // the raw bits are the fragment: no instruction touches the loaded
@@ -174,12 +175,12 @@ __device__ __forceinline__ void load_zB(const E *__restrict__ z, int64_t tok, bo
 
 // Tap-k filters of 16 tokens: acc[p][e] at lane (q, j) is the tap-k weight of
 // slot m = 4p+e of the token whose z fragment is bz.
-template <typename E, int W, int GPV>
+template <typename E, int W, int GPV, int RB>
 __device__ __forceinline__ void gen_tap(
-    const typename WFrag<sizeof(E) == 2>::T (&a)[LrGeo<E, W, GPV>::NP][LrGeo<E, W, GPV>::KS],
-    const typename WFrag<sizeof(E) == 2>::T (&bz)[LrGeo<E, W, GPV>::KS],
-    f32x4 (&acc)[LrGeo<E, W, GPV>::NP]) {
-  using Gm = LrGeo<E, W, GPV>;
+    const typename WFrag<sizeof(E) == 2>::T (&a)[LrGeo<E, W, GPV, RB>::NP][LrGeo<E, W, GPV, RB>::KS],
+    const typename WFrag<sizeof(E) == 2>::T (&bz)[LrGeo<E, W, GPV, RB>::KS],
+    f32x4 (&acc)[LrGeo<E, W, GPV, RB>::NP]) {
+  using Gm = LrGeo<E, W, GPV, RB>;
 #pragma unroll
   for (int p = 0; p < Gm::NP; ++p) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -213,12 +214,12 @@ template <typename E, int W, int GPV> struct LrFwdGeo {
 
 // Packed rows (VL): taps k >= 1 of a token beyond its document position are
 // zeroed right after the filters are formed, before any use.
-template <typename E, int W, int GPV, bool ACT, bool VL>
+template <typename E, int W, int GPV, bool ACT, bool VL, int RB>
 __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
     const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U,
     const int32_t *__restrict__ pos, E *__restrict__ y, int T, int D, int R, int TC,
     int nchunk, int ncb, float rho) {
-  using Gm = LrGeo<E, W, GPV>;
+  using Gm = LrGeo<E, W, GPV, RB>;
   using Fg = LrFwdGeo<E, W, GPV>;
   constexpr int V = Gm::V, NU = Gm::NU, NP = Gm::NP, KS = Gm::KS;
   constexpr int XR = Fg::XR, SP = Fg::SP, VPR = Fg::VPR, RPP = Fg::RPP, NPASS = Fg::NPASS;
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
   };
 
   typename WFrag<Gm::BF>::T aw[W][NP][KS];
-  load_wA<E, W, GPV>(U, GW, R, cw, D, lane, aw);
+  load_wA<E, W, GPV, RB>(U, GW, R, cw, D, lane, aw);
 
   // the 16 rows before the chunk (zero before the sequence)
 #pragma unroll
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
     if (t + 16 * PF < t1) issue(t + 16 * PF, sl);  // workgroup-uniform
     f32x4 wacc[W][NP];
 #pragma unroll
-    for (int k = 0; k < W; ++k) gen_tap<E, W, GPV>(aw[k], bz, wacc[k]);
+    for (int k = 0; k < W; ++k) gen_tap<E, W, GPV, RB>(aw[k], bz, wacc[k]);
     if constexpr (VL) {
 #pragma unroll
       for (int k = 1; k < W; ++k)
@@ -376,14 +377,14 @@ constexpr uint32_t kOOB = 0x80000000u;
 // each touched once per call)
 constexpr int kNT = 2;
 
-template <typename E, int W, int GPV> struct LrBwdGeo {
-  using Gm = LrGeo<E, W, GPV>;
+template <typename E, int W, int GPV, int RB> struct LrBwdGeo {
+  using Gm = LrGeo<E, W, GPV, RB>;
   static constexpr int RS = (int)sizeof(E);
   static constexpr int XP = Gm::CB * 4 + 16;   // x ring row pitch (fp32)
   static constexpr int DP = Gm::CB * 4 + 16;   // ds ring row pitch (fp32)
   static constexpr int SP = Gm::CB * RS + 16;  // dx staging row pitch
-  // z ring row: 16 ranks + 8 bytes, so 16 lanes reading 16 rows hit distinct banks
-  static constexpr int ZP = 16 * RS + 8;
+  // z ring row: 16 * RB ranks + 8 bytes, so 16 lanes reading 16 rows hit distinct banks
+  static constexpr int ZP = 16 * RB * RS + 8;
   static constexpr int VPR = Gm::CB / Gm::V;
   static constexpr int RPP = kLrThreads / VPR;
   static constexpr int NPASS = 16 / RPP;
@@ -401,12 +402,12 @@ template <typename E, int W, int GPV> struct LrBwdGeo {
   static constexpr int bytes = o_pos + 32 * 4;
 };
 
-template <typename E, int W, int GPV>
+template <typename E, int W, int GPV, int RB>
 __device__ __forceinline__ void gen_tap_init(
-    const typename WFrag<sizeof(E) == 2>::T (&a)[LrGeo<E, W, GPV>::NP][LrGeo<E, W, GPV>::KS],
-    const typename WFrag<sizeof(E) == 2>::T (&bz)[LrGeo<E, W, GPV>::KS],
-    f32x4 (&acc)[LrGeo<E, W, GPV>::NP], float init) {
-  using Gm = LrGeo<E, W, GPV>;
+    const typename WFrag<sizeof(E) == 2>::T (&a)[LrGeo<E, W, GPV, RB>::NP][LrGeo<E, W, GPV, RB>::KS],
+    const typename WFrag<sizeof(E) == 2>::T (&bz)[LrGeo<E, W, GPV, RB>::KS],
+    f32x4 (&acc)[LrGeo<E, W, GPV, RB>::NP], float init) {
+  using Gm = LrGeo<E, W, GPV, RB>;
 #pragma unroll
   for (int p = 0; p < Gm::NP; ++p) {
     f32x4 c = {init, init, init, init};
@@ -418,8 +419,10 @@ __device__ __forceinline__ void gen_tap_init(
 
 // Three waves per SIMD where the compiler fits that without spilling, fewer
 // otherwise; the set was read off the kernel resource-usage report.
-template <typename E, int W, int GPV, bool VL>
+template <typename E, int W, int GPV, bool VL, int RB>
 constexpr int lr_bwd_min_waves() {
+  // more than 16 ranks: filter fragments of every rank block stay resident
+  if constexpr (RB > 1) return 1;
   // packed rows' position ring takes the per-channel W = 4 case over
   if constexpr (VL && sizeof(E) == 2 && GPV == 8 && W == 4) return 2;
   if constexpr (sizeof(E) == 2)
@@ -432,19 +435,23 @@ constexpr int lr_bwd_min_waves() {
 // Packed rows (VL): a 32-entry ring of document positions beside the z ring;
 // a tap k >= 1 of token t is zeroed where k > pos[t], in the filters of dx and
 // of the SiLU recomputation and in dw (hence in dz and dU).
-template <typename E, int W, int GPV, bool VL>
-__global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) void lr_bwd_kernel(
+//
+// More than 16 ranks (RB > 1): the filters use every rank, and dz and dU are
+// formed for one block of 16 ranks, rb0, per launch; the launcher runs one
+// pass per block, the first of which also writes dx (do_dx).
+template <typename E, int W, int GPV, bool VL, int RB>
+__global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())) void lr_bwd_kernel(
     const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U,
     const E *__restrict__ dy, const int32_t *__restrict__ pos, E *__restrict__ dx,
     float *__restrict__ dzp, float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk,
-    int ncb, int64_t N, float rho, int act) {
-  using Gm = LrGeo<E, W, GPV>;
-  using Bg = LrBwdGeo<E, W, GPV>;
+    int ncb, int64_t N, float rho, int act, int rb0, int do_dx) {
+  using Gm = LrGeo<E, W, GPV, RB>;
+  using Bg = LrBwdGeo<E, W, GPV, RB>;
   constexpr bool BF = Gm::BF;
   constexpr int V = Gm::V, NU = Gm::NU, NG = Gm::NG, NP = Gm::NP, NS = Gm::NS, KS = Gm::KS;
   constexpr int NDZ = BF ? (NS + 7) / 8 : NS;
   constexpr int NRB = Bg::nrb;
-  constexpr int RP = 16, RS = Bg::RS;
+  constexpr int RP = 16 * RB, RS = Bg::RS;
   constexpr int XP = Bg::XP, DP = Bg::DP, SP = Bg::SP, ZP = Bg::ZP, VPR = Bg::VPR, RPP = Bg::RPP,
                 NPASS = Bg::NPASS;
   constexpr int PF = 1;  // loads one step ahead: a step outlasts the load latency
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
     const E *zr = zrow(tok);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (BF) f[ks] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(zr + 4 * q));
+      if constexpr (BF) f[ks] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(zr + 16 * ks + 4 * q));
       else f[ks] = zr[ks * 4 + q];
     }
   };
@@ -494,20 +501,33 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
   auto slab = [&](const E *base, int t, int lim) {
     return mk_rsrc(base + (seq + t) * (int64_t)D, (int64_t)(min(lim, t + 16) - t) * D * RS);
   };
-  const bool z_on = tid < 16 * R;
-  const uint32_t zoff = z_on ? (uint32_t)tid * RS : kOOB;
-  const int zr_tok = tid / (R > 0 ? R : 1), zr_rank = tid - zr_tok * (R > 0 ? R : 1);
+  // the 16 x R values of a z slab, RB per thread: value zi = tid + 256 * i
+  uint32_t zoff[RB];
+  int zslot[RB];  // element offset of the value in a z ring row block, or -1
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    const int zi = tid + kLrThreads * i;
+    const bool on = zi < 16 * R;
+    zoff[i] = on ? (uint32_t)zi * RS : kOOB;
+    const int tok = zi / (R > 0 ? R : 1), rank = zi - tok * (R > 0 ? R : 1);
+    zslot[i] = on ? tok * (ZP / RS) + rank : -1;
+  }
   auto zslab = [&](int t, int lim) {
     return mk_rsrc(z + (seq + t) * (int64_t)R, (int64_t)(min(lim, t + 16) - t) * R * RS);
+  };
+  // ring row of token t0 + 16 m + r is (t0 + 16 m + r) & 31: the 16 rows of a
+  // slab starting at a multiple of 16 are contiguous in the ring
+  auto zput = [&](int t, int i, E v) {
+    if (zslot[i] >= 0) reinterpret_cast<E *>(zring + (t & 31) * ZP)[zslot[i]] = v;
   };
 
   for (int i = tid; i < 32 * ZP / 4; i += kLrThreads) reinterpret_cast<uint32_t *>(zring)[i] = 0u;
 
   typename WFrag<BF>::T aw[W][NP][KS];
-  load_wA<E, W, GPV>(U, GW, R, cw, D, lane, aw);
+  load_wA<E, W, GPV, RB>(U, GW, R, cw, D, lane, aw);
   typename DzFrag<BF>::T adz[NDZ];
   {
-    const int qa = lane >> 4, r = lane & 15;
+    const int qa = lane >> 4, r = 16 * rb0 + (lane & 15);
 #pragma unroll
     for (int s = 0; s < NDZ; ++s) {
       if constexpr (BF) {
@@ -548,16 +568,17 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
       for (int h = 0; h < V / 4; ++h) dst[h] = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
     }
     const brsrc rz = zslab(tb, tb < 0 ? tb : T);
-    if (z_on) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
       E v;
-      if constexpr (BF) v = (E)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
-      else v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, 0, 0));
-      reinterpret_cast<E *>(zring + ((tb + zr_tok) & 31) * ZP)[zr_rank] = v;
+      if constexpr (BF) v = (E)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff[i], 0, 0);
+      else v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[i], 0, 0));
+      zput(tb, i, v);
     }
   }
 
   uint4 xn[PF][NPASS], dyn[PF][NPASS];
-  E zn[PF];
+  E zn[PF][RB];
   int pn[PF];
   auto issue = [&](int st, int sl) {
     const int t = t0 + 16 * st;
@@ -577,8 +598,11 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
         xn[sl][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff[p], 0, kNT));
     }
     const brsrc rz = zslab(t, T);
-    if constexpr (BF) zn[sl] = (E)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
-    else zn[sl] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, 0, 0));
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if constexpr (BF) zn[sl][i] = (E)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff[i], 0, 0);
+      else zn[sl][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[i], 0, 0));
+    }
   };
   auto fill = [&](int st, int sl) {
     const int t = t0 + 16 * st;
@@ -599,7 +623,8 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
         for (int h = 0; h < V / 4; ++h) xd[h] = f32x4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
       }
     }
-    if (z_on) reinterpret_cast<E *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn[sl];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) zput(t, i, zn[sl][i]);
     if (VL && tid < 16) pring[(t + tid) & 31] = pn[sl];
   };
 
@@ -617,7 +642,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
   // rows then never waits for stores issued after those loads.
   auto flush = [&](int st) {
     const int t = t0 + 16 * st;
-    if (st > 0) {
+    if (st > 0 && do_dx) {
       const brsrc rdx = slab(dx, t - 16, t1);
 #pragma unroll
       for (int p = 0; p < NPASS; ++p) {
@@ -629,7 +654,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
       f32x4 s4 = *reinterpret_cast<const f32x4 *>(dzbuf + lane * 4);
 #pragma unroll
       for (int w2 = 1; w2 < 4; ++w2) s4 += *reinterpret_cast<const f32x4 *>(dzbuf + (w2 * 64 + lane) * 4);
-      *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + t + j) * RP + 4 * q) = s4;
+      *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + t + j) * RP + 16 * rb0 + 4 * q) = s4;
     }
   };
   auto step = [&](int st, int sl) {
@@ -660,7 +685,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
       zfrag(tau, bz);
       f32x4 wacc[W][NP];
 #pragma unroll
-      for (int k = 0; k < W; ++k) gen_tap<E, W, GPV>(aw[k], bz, wacc[k]);
+      for (int k = 0; k < W; ++k) gen_tap<E, W, GPV, RB>(aw[k], bz, wacc[k]);
       if constexpr (VL) {
         const int pj = pring[tau & 31];
 #pragma unroll
@@ -697,14 +722,14 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
     }
     __builtin_amdgcn_wave_barrier();
     // dx of the previous tile: dx[t'] = rho dy[t'] + sum_k w[t'+k,.,k] ds[t'+k]
-    if (st > 0) {
+    if (st > 0 && do_dx) {
       const int tp = t - 16 + j;
 #pragma unroll
       for (int k = 0; k < W; ++k) {
         typename WFrag<BF>::T bzs[KS];
         zfrag(tp + k, bzs);
         f32x4 wk[NP];
-        gen_tap_init<E, W, GPV>(aw[k], bzs, wk, k == 0 ? rho_tap : 0.f);
+        gen_tap_init<E, W, GPV, RB>(aw[k], bzs, wk, k == 0 ? rho_tap : 0.f);
         if (VL && k > 0 && k > pring[(tp + k) & 31])
 #pragma unroll
           for (int p = 0; p < NP; ++p) wk[p] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -776,15 +801,16 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
       *reinterpret_cast<f32x4 *>(dzbuf + (wave * 64 + lane) * 4) = dzacc;
       // dU^T += dw^T z, one 16-row block (slots 4a..4a+3 of every quarter) at a time
       const int qa = lane >> 4, n = lane & 15;
-      typename WFrag<BF>::T bzt[KS];
+      // z of rank 16 * rb0 + n (this pass's block)
+      typename WFrag<BF>::T bzt[BF ? 1 : 4];
       if constexpr (BF) {
         s16x4 f;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) f[e2] = (short)zrow(t + 4 * qa + e2)[n];
+        for (int e2 = 0; e2 < 4; ++e2) f[e2] = (short)zrow(t + 4 * qa + e2)[16 * rb0 + n];
         bzt[0] = f;
       } else {
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) bzt[s4] = zrow(t + 4 * s4 + qa)[n];
+        for (int s4 = 0; s4 < 4; ++s4) bzt[s4] = zrow(t + 4 * s4 + qa)[16 * rb0 + n];
       }
 #pragma unroll
       for (int a = 0; a < NRB; ++a) {
@@ -836,7 +862,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL>())) vo
       for (int e = 0; e < 4; ++e) {
         const int col = slot_col<E, W, GPV>(cw, e, sg / NG, sg % NG, D);
         if (col < 0) continue;
-        dst[(int64_t)n * GW + col] = accU[a][e];
+        dst[(int64_t)(16 * rb0 + n) * GW + col] = accU[a][e];
       }
     }
   }

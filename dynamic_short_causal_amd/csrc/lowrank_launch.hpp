@@ -8,7 +8,7 @@
 
 namespace dsc {
 
-template <typename E, int W, int GPV, bool ACT, bool VL>
+template <typename E, int W, int GPV, bool ACT, bool VL, int RB>
 static hipError_t launch_lr_fwd(const LrArgs &a) {
   using Gm = LrGeo<E, W, GPV>;
   hipStream_t s = (hipStream_t)a.stream;
@@ -19,7 +19,7 @@ static hipError_t launch_lr_fwd(const LrArgs &a) {
   const int64_t nblocks = a.B * nchunk * (int64_t)ncb;
   if (nblocks == 0) return hipSuccess;
   constexpr int smem = LrFwdGeo<E, W, GPV>::bytes;
-  hipLaunchKernelGGL((lr_fwd_kernel<E, W, GPV, ACT, VL>), dim3((unsigned)nblocks),
+  hipLaunchKernelGGL((lr_fwd_kernel<E, W, GPV, ACT, VL, RB>), dim3((unsigned)nblocks),
                      dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
                      (const E *)a.U, a.pos, (E *)a.y, (int)a.T, (int)a.D, a.R, TC, nchunk, ncb,
                      rho);
@@ -37,7 +37,7 @@ static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
   hipStream_t s = (hipStream_t)a.stream;
   const float rho = a.residual ? 1.f : 0.f;
   const LrBwdPlan p = lr_bwd_plan(a.B, a.T, a.D, a.W, a.H, a.R, a.bf16, true);
-  if (p.cb != kClCB || !lr_bwd_uses_cl(a.H, a.bf16, a.act)) return hipErrorInvalidValue;
+  if (p.cb != kClCB || !lr_bwd_uses_cl(a.H, a.R, a.bf16, a.act)) return hipErrorInvalidValue;
   float *dzp = (float *)a.ws;
   float *dUp = (float *)((char *)a.ws + p.dz_part);
   const int64_t nblocks = a.B * p.nchunk * p.ncb;
@@ -54,9 +54,11 @@ static hipError_t launch_lr_bwd_cl(const LrArgs &a) {
   return launch_lr_reduce<bf16>(a, p, dzp, dUp);
 }
 
-template <typename E, int W, int GPV, bool VL>
+// One launch of lr_bwd_kernel per block of 16 ranks (the first also writes
+// dx), then the fixed-order reduction of every block's partials.
+template <typename E, int W, int GPV, bool VL, int RB>
 static hipError_t launch_lr_bwd(const LrArgs &a) {
-  if (lr_bwd_uses_cl(a.H, sizeof(E) == 2, a.act)) {  // bf16, H == 1, no SiLU
+  if (RB == 1 && lr_bwd_uses_cl(a.H, a.R, sizeof(E) == 2, a.act)) {  // bf16, H = 1, R <= 16, no SiLU
     return launch_lr_bwd_cl<W, VL>(a);
   } else {
     hipStream_t s = (hipStream_t)a.stream;
@@ -66,13 +68,13 @@ static hipError_t launch_lr_bwd(const LrArgs &a) {
     float *dzp = (float *)a.ws;
     float *dUp = (float *)((char *)a.ws + p.dz_part);
     const int64_t nblocks = a.B * p.nchunk * p.ncb;
-    if (nblocks > 0) {
-      constexpr int smem = LrBwdGeo<E, W, GPV>::bytes;
-      hipLaunchKernelGGL((lr_bwd_kernel<E, W, GPV, VL>), dim3((unsigned)nblocks),
+    for (int rb0 = 0; nblocks > 0 && rb0 < RB; ++rb0) {
+      constexpr int smem = LrBwdGeo<E, W, GPV, RB>::bytes;
+      hipLaunchKernelGGL((lr_bwd_kernel<E, W, GPV, VL, RB>), dim3((unsigned)nblocks),
                          dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
                          (const E *)a.U, (const E *)a.dy, a.pos, (E *)a.dx, dzp, dUp,
                          (int)a.T, (int)a.D, a.R, p.tc, (int)p.nchunk, (int)p.ncb, N, rho,
-                         a.act ? 1 : 0);
+                         a.act ? 1 : 0, rb0, rb0 == 0 ? 1 : 0);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -97,42 +99,44 @@ static hipError_t launch_lr_reduce(const LrArgs &a, const LrBwdPlan &p, const fl
   return hipGetLastError();
 }
 
-// one 16-row rank block: the argument checks admit R <= 16 only
-template <typename E, int W, int GPV, bool BWD, bool VL>
+// RB blocks of 16 ranks (the dispatcher picks RB = 1, 2 or 4 for R <= 16, 32, 64)
+template <typename E, int W, int GPV, int RB, bool BWD, bool VL>
 static hipError_t lr_rb(const LrArgs &a) {
   if constexpr (BWD) {
-    return launch_lr_bwd<E, W, GPV, VL>(a);
+    return launch_lr_bwd<E, W, GPV, VL, RB>(a);
   } else {
-    return a.act ? launch_lr_fwd<E, W, GPV, true, VL>(a) : launch_lr_fwd<E, W, GPV, false, VL>(a);
+    return a.act ? launch_lr_fwd<E, W, GPV, true, VL, RB>(a)
+                 : launch_lr_fwd<E, W, GPV, false, VL, RB>(a);
   }
 }
 
-template <typename E, int W, bool BWD, bool VL>
+template <typename E, int W, int RB, bool BWD, bool VL>
 static hipError_t lr_gpv(const LrArgs &a) {
   constexpr int V = Vw<E>::n;
   switch (V / a.H) {
-    case 1: return lr_rb<E, W, 1, BWD, VL>(a);
-    case 2: return lr_rb<E, W, 2, BWD, VL>(a);
-    case 4: return lr_rb<E, W, 4, BWD, VL>(a);
+    case 1: return lr_rb<E, W, 1, RB, BWD, VL>(a);
+    case 2: return lr_rb<E, W, 2, RB, BWD, VL>(a);
+    case 4: return lr_rb<E, W, 4, RB, BWD, VL>(a);
     default:
-      if constexpr (V == 8) return lr_rb<E, W, 8, BWD, VL>(a);
+      if constexpr (V == 8) return lr_rb<E, W, 8, RB, BWD, VL>(a);
       return hipErrorInvalidValue;
   }
 }
 
-// VL: rows packed with documents (a.pos set); instantiated in their own
-// translation units so the two builds compile in parallel
-template <typename E, bool BWD, bool VL>
-hipError_t lr_dispatch(const LrArgs &a) {
+// VL: rows packed with documents (a.pos set).  Each (dtype, direction, VL,
+// RB) set is instantiated in a translation unit of its own so they compile
+// in parallel.
+template <typename E, int RB, bool BWD, bool VL>
+hipError_t lr_dispatch_rb(const LrArgs &a) {
   switch (a.W) {
-    case 1: return lr_gpv<E, 1, BWD, VL>(a);
-    case 2: return lr_gpv<E, 2, BWD, VL>(a);
-    case 3: return lr_gpv<E, 3, BWD, VL>(a);
-    case 4: return lr_gpv<E, 4, BWD, VL>(a);
-    case 5: return lr_gpv<E, 5, BWD, VL>(a);
-    case 6: return lr_gpv<E, 6, BWD, VL>(a);
-    case 7: return lr_gpv<E, 7, BWD, VL>(a);
-    case 8: return lr_gpv<E, 8, BWD, VL>(a);
+    case 1: return lr_gpv<E, 1, RB, BWD, VL>(a);
+    case 2: return lr_gpv<E, 2, RB, BWD, VL>(a);
+    case 3: return lr_gpv<E, 3, RB, BWD, VL>(a);
+    case 4: return lr_gpv<E, 4, RB, BWD, VL>(a);
+    case 5: return lr_gpv<E, 5, RB, BWD, VL>(a);
+    case 6: return lr_gpv<E, 6, RB, BWD, VL>(a);
+    case 7: return lr_gpv<E, 7, RB, BWD, VL>(a);
+    case 8: return lr_gpv<E, 8, RB, BWD, VL>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -46,7 +46,7 @@
  *                        call, or more than 2^38 elements in x (far beyond
  *                        one GPU's memory; the bound keeps launch grids
  *                        below 2^31 workgroups);
- *   DSC_ERR_UNSUPPORTED  W outside 1..8, R outside 1..16, an unknown flag or
+ *   DSC_ERR_UNSUPPORTED  W outside 1..8, R outside 1..64, an unknown flag or
  *                        dtype, or a tying factor H the kernels do not tile
  *                        (head-wise: H divides the vector width, or H is the
  *                        vector width times a power of two up to 64; low-rank:

@@ -100,9 +100,10 @@ def test_after_prompt(dsc, orc, T0):
          R=16)
 
 
-@pytest.mark.parametrize("R", [1, 7, 16])
+@pytest.mark.parametrize("R", [1, 7, 16, 17, 40, 64])
 def test_ranks(dsc, orc, R):
     roll(dsc, orc, True, 2, 6, 64, 4, 1, torch.bfloat16, True, False, 6800 + R, R=R)
+    roll(dsc, orc, True, 3, 5, 64, 4, 2, torch.float32, True, True, 6850 + R, R=R)
 
 
 def test_single_vector_and_large_batch(dsc, orc):

@@ -54,10 +54,32 @@ def test_widths(dsc, orc, W):
     run_case(dsc, orc, 1, 70, 128, W, 2, 16, torch.float32, False, True, 7300 + W)
 
 
-@pytest.mark.parametrize("R", [1, 3, 8, 12, 16])
+@pytest.mark.parametrize("R", [1, 3, 8, 12, 16, 17, 24, 32, 33, 48, 64])
 def test_ranks(dsc, orc, R):
+    """Ranks within one 16-rank block and across two and four (the backward
+    then runs one pass per block)."""
     run_case(dsc, orc, 2, 45, 256, 4, 1, R, torch.bfloat16, True, False, 7400 + R)
     run_case(dsc, orc, 1, 45, 64, 4, 4, R, torch.float32, False, False, 7500 + R)
+
+
+@pytest.mark.parametrize("R", [20, 64])
+@pytest.mark.parametrize("H,act", [(1, True), (8, False), (2, True)])
+def test_many_ranks_tied_and_silu(dsc, orc, R, H, act):
+    run_case(dsc, orc, 2, 150, 512 + 8 * 16 * H, 4, H, R, torch.bfloat16, True, act,
+             7550 + R + 10 * H)
+
+
+@pytest.mark.parametrize("W,H,dt", [(8, 1, "bf16"), (7, 1, "bf16"), (8, 2, "f32"), (1, 1, "f32")])
+def test_many_ranks_widths(dsc, orc, W, H, dt):
+    """The widest filters at 64 ranks (the largest resident fragment sets)."""
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    run_case(dsc, orc, 2, 70, 256, W, H, 64, dtype, True, dt == "bf16", 7580 + W + H)
+
+
+@pytest.mark.parametrize("B,T", [(1, 1), (2, 3), (1, 17)])
+def test_many_ranks_short_sequences(dsc, orc, B, T):
+    run_case(dsc, orc, B, T, 128, 4, 1, 48, torch.bfloat16, True, True, 7590 + T)
+    run_case(dsc, orc, B, T, 64, 4, 2, 33, torch.float32, True, False, 7595 + T)
 
 
 @pytest.mark.parametrize("residual,act", [(False, False), (True, False), (False, True),

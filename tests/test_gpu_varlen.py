@@ -97,6 +97,14 @@ def test_lowrank_tying(dsc, orc, H, dtype):
             packing(2, 150, 7 + H, 6))
 
 
+@pytest.mark.parametrize("R,W,H,dtype", [(32, 4, 1, torch.bfloat16), (64, 8, 1, torch.bfloat16),
+                                         (40, 3, 8, torch.bfloat16), (64, 4, 1, torch.float32)],
+                         ids=["bf16-R32", "bf16-R64-W8", "bf16-R40-H8", "f32-R64"])
+def test_lowrank_many_ranks(dsc, orc, R, W, H, dtype):
+    lr_case(dsc, orc, 2, 97, 256, W, H, R, dtype, True, dtype == torch.bfloat16, 9250 + R + W,
+            packing(2, 97, 40 + R, 6))
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 5, 8])
 def test_lowrank_widths_silu(dsc, orc, W):
     lr_case(dsc, orc, 2, 97, 256, W, 1, 16, torch.bfloat16, True, True, 9300 + W,
