@@ -924,21 +924,25 @@ def main():
                      / args.steps for i, n in enumerate(names)}
 
     # Each op alone: blocks of 10 back-to-back calls between two events, the
-    # calls alternating between the op's inputs and a second copy of them (the
-    # two sets exceed the last-level cache), median of 5 blocks.  This spreads
+    # calls alternating between two complete sets of the op's tensors (inputs,
+    # outputs and workspace: more than the last-level cache holds, so neither
+    # set is cached when its turn comes), median of 5 blocks.  This spreads
     # the cost of the event packets over the block, so the figure is the one a
     # kernel trace gives (the roofline entry uses it).
     print("bench: timing each op in blocks", file=sys.stderr, flush=True)
-    xa2, wa2 = cp(xa), cp(wa)
+    xa2, wa2, y_h2 = cp(xa), cp(wa), torch.empty_like(y_h)
     xb2, wb2, dyb2 = cp(xb), cp(wb), cp(dyb)
-    xc2, zc2 = cp(xc), cp(zc)
+    dx_h2, dw_h2 = torch.empty_like(dx_h), torch.empty_like(dw_h)
+    xc2, zc2, y_l2 = cp(xc), cp(zc), torch.empty_like(y_l)
     xd2, zd2, dyd2 = cp(xd), cp(zd), cp(dyd)
+    dx_l2, dz2, dU2, ws2 = (torch.empty_like(dx_l), torch.empty_like(dz), torch.empty_like(dU),
+                            torch.empty_like(ws))
     alt = {
-        "headwise_fwd": lambda: dsc.dsc_headwise_fwd(xa2, wa2, y_h, Hh, True, False, stream),
-        "headwise_bwd": lambda: dsc.dsc_headwise_bwd(xb2, wb2, dyb2, dx_h, dw_h, Hh, True, False,
+        "headwise_fwd": lambda: dsc.dsc_headwise_fwd(xa2, wa2, y_h2, Hh, True, False, stream),
+        "headwise_bwd": lambda: dsc.dsc_headwise_bwd(xb2, wb2, dyb2, dx_h2, dw_h2, Hh, True, False,
                                                      stream),
-        "lowrank_fwd": lambda: dsc.dsc_lowrank_fwd(xc2, zc2, Uc, y_l, W, Hl, True, False, stream),
-        "lowrank_bwd": lambda: dsc.dsc_lowrank_bwd(xd2, zd2, Ud, dyd2, dx_l, dz, dU, ws, W, Hl,
+        "lowrank_fwd": lambda: dsc.dsc_lowrank_fwd(xc2, zc2, Uc, y_l2, W, Hl, True, False, stream),
+        "lowrank_bwd": lambda: dsc.dsc_lowrank_bwd(xd2, zd2, Ud, dyd2, dx_l2, dz2, dU2, ws2, W, Hl,
                                                    True, False, stream),
     }
     block_ms = {}
@@ -953,7 +957,8 @@ def main():
             torch.cuda.synchronize()
             per.append(e0.elapsed_time(e1) / 10)
         block_ms[n] = sorted(per)[2]
-    del xa2, wa2, xb2, wb2, dyb2, xc2, zc2, xd2, zd2, dyd2
+    del xa2, wa2, y_h2, xb2, wb2, dyb2, dx_h2, dw_h2, xc2, zc2, y_l2, xd2, zd2, dyd2
+    del dx_l2, dz2, dU2, ws2
 
     # a plain device copy of 1 GiB for the achievable-bandwidth context
     src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)

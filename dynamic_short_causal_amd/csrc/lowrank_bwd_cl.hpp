@@ -95,7 +95,6 @@ __device__ __forceinline__ void store_floats(float *p, const float (&v)[N]) {
 
 constexpr int kClWaves = kLrClWaves;           // waves per workgroup
 constexpr int kClNG = kLrClNG;                 // 16-channel groups per wave
-constexpr int kClPF = 1;                       // steps of x, dy, z loads in flight
 constexpr int kClThreads = 64 * kClWaves;
 constexpr int kClCB = kLrClCB;                 // channels per workgroup
 constexpr int kClVPR = kClCB / 8;              // 16-byte vectors per row of the block
@@ -124,8 +123,8 @@ template <int W> struct LrBwdClGeo {
 // kernel resource-usage report; the register count grows with W).
 template <int W, bool VL>
 constexpr int lr_bwd_cl_min_waves() {
-  // the position masks of packed rows tip W = 4 and 8 over
-  if constexpr (W == 8) return 1;
+  // the position masks of packed rows tip W = 4, 7 and 8 over
+  if constexpr (W == 8 || (VL && W == 7)) return 1;
   if constexpr (VL && W == 4) return 2;
   return W <= 4 ? 3 : 2;
 }
@@ -216,7 +215,6 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
     for (int k = 0; k < W; ++k) accU[u][k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int tiles = (t1 - t0 + 15) / 16;
-  const int nsteps = tiles + 1;
   __syncthreads();
   if (c_x) {  // x of the 16 tokens before the chunk (zero before the sequence)
     const int tb = t0 - 16;
@@ -229,36 +227,38 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
     return base + row * XP + (col0 + 4 * (n & 3)) * 2;
   };
 
-  // loads of step st go to slot st % kClPF, kClPF steps ahead
-  uint4 xn[kClPF], dyn[kClPF];
-  bf16 zn[kClPF];
-  int pn[kClPF];
-  auto issue = [&](int st, int sl) {  // sl: compile-time after unrolling
+  // Loads of step st are issued one step ahead, into registers.  (Two or
+  // three steps ahead needed registers beyond three waves per SIMD and ran
+  // slower.)  The last step (`halo`) loads only dy, z and positions: it
+  // completes dx of the chunk's last tile.
+  uint4 xn, dyn;
+  bf16 zn;
+  int pn;
+  auto issue = [&](int st) {
     const int t = t0 + 16 * st;
     const bool halo = st == tiles;
     if constexpr (VL) {
       const brsrc rp = mk_rsrc(pos + seq + t, (int64_t)(min(T, t + 16) - t) * 4);
-      pn[sl] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, tid < 16 ? (uint32_t)tid * 4 : kOOB, 0, 0);
+      pn = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, tid < 16 ? (uint32_t)tid * 4 : kOOB, 0, 0);
     }
     const brsrc rz = slab(z, t, T, R, R);
-    zn[sl] = (bf16)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
+    zn = (bf16)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
     if (c_dy) {
       const brsrc rd = slab(dy, t, T, D, D);
-      dyn[sl] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, coff, 0, kNT));
+      dyn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rd, coff, 0, kNT));
     }
     if (c_x && !halo) {
       const brsrc rx = slab(x, t, T, D, D);
-      xn[sl] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, coff, 0, kNT));
+      xn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, coff, 0, kNT));
     }
   };
-  auto fill = [&](int st, int sl) {
+  auto fill = [&](int st, bool halo) {
     const int t = t0 + 16 * st;
-    const bool halo = st == tiles;
     const int row = (t + cr) & 31;
-    if (c_x && !halo) *reinterpret_cast<uint4 *>(xring + row * XP + cv * 16) = xn[sl];
-    if (c_dy) *reinterpret_cast<uint4 *>(dyring + row * XP + cv * 16) = dyn[sl];
-    if (z_on) reinterpret_cast<bf16 *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn[sl];
-    if (VL && tid < 16) pring[(t + tid) & 31] = pn[sl];
+    if (c_x && !halo) *reinterpret_cast<uint4 *>(xring + row * XP + cv * 16) = xn;
+    if (c_dy) *reinterpret_cast<uint4 *>(dyring + row * XP + cv * 16) = dyn;
+    if (z_on) reinterpret_cast<bf16 *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn;
+    if (VL && tid < 16) pring[(t + tid) & 31] = pn;
   };
 
   // The device stores of step st (dx of tile st-1 from the staging rows, dz of
@@ -285,12 +285,15 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
   // lane's own four dy values of the step before (the first dy quad of its dx)
   const float rho_tap = rho;
   float dyp[NG][4];
-  auto step = [&](int st, int sl) {
+  // halo_c: std::true_type for the last step (tokens after the chunk, dx
+  // only).  Resolving it at compile time keeps every dU accumulation of the
+  // main steps unconditional, so the accumulators stay in place across them.
+  auto step = [&](int st, auto halo_c) {
+    constexpr bool halo = decltype(halo_c)::value;
     const int t = t0 + 16 * st;
-    const bool halo = st == tiles;
-    fill(st, sl);
+    fill(st, halo);
     if (st > 0) flush(st - 1);
-    if (st + kClPF < nsteps) issue(st + kClPF, sl);
+    if (!halo) issue(st + 1);
     __syncthreads();  // (1) rings of this step written; staging and dz tiles of the last read
     constexpr int X0 = 4 * NHQ;
     float dyc[NG][4], xw[NG][4 * NHQ + 4];
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
     for (int u = 0; u < NG; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) dyp[u][e] = dyc[u][e];
-    if (!halo) {
+    if constexpr (!halo) {
       const s16x4 azt = tr16(zring + ((t + 4 * q + (n >> 2)) & 31) * ZP + 8 * (n & 3));
       // chunk read by this lane; chunk c is stored at slot c ^ (bit 5 of c ->
       // bit 3), so the 32 chunks of one read pass sit on 32 distinct bank pairs
@@ -398,15 +401,10 @@ __global__ __launch_bounds__(kClThreads, (lr_bwd_cl_min_waves<W, VL>())) void lr
     }
     __syncthreads();  // (2) staging, dz tiles and ring reads of this step complete
   };
-#pragma unroll
-  for (int p = 0; p < kClPF; ++p)
-    if (p < nsteps) issue(p, p);
-  for (int st = 0; st < nsteps; st += kClPF) {
-#pragma unroll
-    for (int p = 0; p < kClPF; ++p)
-      if (st + p < nsteps) step(st + p, p);
-  }
-  flush(nsteps - 1);
+  issue(0);
+  for (int st = 0; st < tiles; ++st) step(st, std::false_type{});
+  step(tiles, std::true_type{});
+  flush(tiles);
   // dU partial of this chunk: lane (q, n) holds ranks 4q..4q+3 of channel c,
   // every tap; a rank row of U has channel c's W taps contiguously
   float *dst = dUp + (int64_t)(b * nchunk + chunk) * RP * GW;

@@ -426,9 +426,9 @@ constexpr int lr_bwd_min_waves() {
   // packed rows' position ring takes the per-channel W = 4 case over
   if constexpr (VL && sizeof(E) == 2 && GPV == 8 && W == 4) return 2;
   if constexpr (sizeof(E) == 2)
-    return GPV == 8 && W == 8 ? 1
-           : (GPV == 8 && W >= 5) || (GPV == 4 && W == 8) || (VL && GPV == 4 && W == 7) ? 2
-                                                                                         : 3;
+    return (GPV == 8 && W == 8) || (VL && GPV == 8 && W == 7) ? 1
+           : (GPV == 8 && W >= 5) || (GPV == 4 && W >= 7) ? 2
+                                                          : 3;
   else return GPV == 4 && W >= 7 ? 2 : 3;
 }
 
@@ -552,7 +552,6 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
   for (int a = 0; a < NRB; ++a) accU[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int tiles = (t1 - t0 + 15) / 16;
-  const int nsteps = tiles + 1;
   __syncthreads();  // z ring zeroed
   // prologue: x and z of the 16 tokens before the chunk (none before the sequence)
   {
@@ -657,13 +656,18 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
       *reinterpret_cast<f32x4 *>(dzp + ((int64_t)cb * N + seq + t + j) * RP + 16 * rb0 + 4 * q) = s4;
     }
   };
-  auto step = [&](int st, int sl) {
+  // halo_c: std::true_type for the last step (tokens after the chunk, dx
+  // only).  Resolving it at compile time keeps every dU accumulation of the
+  // main steps unconditional, so the accumulators stay in place across them.
+  static_assert(PF == 1, "one step of loads in flight");
+  auto step = [&](int st, auto halo_c) {
+    constexpr bool halo = decltype(halo_c)::value;
+    constexpr int sl = 0;
     const int t = t0 + 16 * st;
-    const bool halo = st == tiles;
     const int tau = t + j;
     fill(st, sl);
     if (st > 0) flush(st - 1);
-    if (st + PF < nsteps) issue(st + PF, sl);
+    if (!halo) issue(st + 1, sl);
     __syncthreads();  // (1) rings and slabs of this step written; staging and dz tiles of the last read
     float dxa[NU][V];
 #pragma unroll
@@ -751,7 +755,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
       for (int u = 0; u < NU; ++u)
         *reinterpret_cast<uint4 *>(dxstage + j * SP + (lcol + (u * 4 + q) * V) * RS) = pack<E>(dxa[u]);
     }
-    if (!halo) {
+    if constexpr (!halo) {
       // filter-gradient slots; a chunk ends inside a tile only at the sequence
       // end, where ds is zero, so no lane needs masking
       float dwv[NS];
@@ -842,15 +846,10 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
     }
     __syncthreads();  // (2) dx staging and dz partials complete; ring reads done
   };
-#pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (p < nsteps) issue(p, p);
-  for (int st = 0; st < nsteps; st += PF) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-      if (st + p < nsteps) step(st + p, p);
-  }
-  flush(nsteps - 1);
+  issue(0, 0);
+  for (int st = 0; st < tiles; ++st) step(st, std::false_type{});
+  step(tiles, std::true_type{});
+  flush(tiles);
   {
     const int qo = lane >> 4, n = lane & 15;
     float *dst = dUp + (int64_t)(b * nchunk + chunk) * RP * GW;
