@@ -133,7 +133,9 @@ SUM_KERNEL = "native::reduce_kernel"     # torch's read-only sum of the same 512
 def op_spans(trace_csv, kernels, calls):
     """Mean span of one call of an op launching `kernels` in order, from the
     per-dispatch timestamps of a --kernel-trace run: first kernel's start to
-    the last kernel's end, over the last `calls` calls (in us)."""
+    the last kernel's end, over the last `calls` - 1 calls (in us).  The first
+    call is left out: the first launch of a kernel loads its code object,
+    which can hold the next kernel of the op back by milliseconds."""
     import csv
     rows = [r for r in csv.DictReader(open(trace_csv))
             if any(k in r["Kernel_Name"] for k in kernels)]
@@ -143,7 +145,7 @@ def op_spans(trace_csv, kernels, calls):
     for a, i in enumerate(first):
         j = first[a + 1] if a + 1 < len(first) else len(rows)
         spans.append((int(rows[j - 1]["End_Timestamp"]) - int(rows[i]["Start_Timestamp"])) / 1e3)
-    spans = spans[-calls:]
+    spans = spans[1:][-max(calls - 1, 1):]
     return sum(spans) / len(spans) if spans else float("nan")
 
 
@@ -205,7 +207,8 @@ def summarize_profiles(d, calls):
               f"{fetch.get(SUM_KERNEL, float('nan')):.0f} KiB, a factor of {ff_sum:.3f}.", "",
               "Op span: one call's first kernel start to last kernel end, from the per-dispatch "
               "timestamps of the trace run (it includes the gap between the kernels of a "
-              "two-kernel op); the benchmark's event times measure this span.", "",
+              "two-kernel op), averaged over all calls but the first, whose launches load the "
+              "code objects; the benchmark's event times measure this span.", "",
               "| op | kernel | calls | avg us | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB |",
               "|---|---|---|---|---|---|---|"]
     for op, ks in OP_KERNELS.items():
