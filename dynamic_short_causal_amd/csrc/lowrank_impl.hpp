@@ -29,17 +29,19 @@
 //
 // Backward per tile (one-tile lag for dx):
 //   * ds = dy (or dy * SiLU'(s), s recomputed from the on-chip filters);
-//   * dx[t] = rho dy[t] + sum_k w[t+k,k] ds[t+k] for the previous tile: the
-//     filters w[t+k,.,k] come from MFMAs fed with z of token t+k (without
-//     SiLU the residual is folded into the tap-0 filter: ds = dy), ds[t+k]
-//     from the ds ring; a final step over the tokens after the chunk (zero
-//     past the sequence end) completes the chunk's last tile;
 //   * dw (on chip only) -> dz^T += U dw^T with 16x16x32 bf16 MFMAs (K = the
 //     lane's slots), summed across the 4 waves in LDS and written as one fp32
 //     partial per channel block;
 //   * dU^T += dw^T z: dw is transposed through LDS, one 16-row block at a
 //     time, so tokens become the K dimension; accumulated over the whole
-//     chunk in registers and written once per chunk as an fp32 partial.
+//     chunk in registers and written once per chunk as an fp32 partial;
+//   * dx[t] = rho dy[t] + sum_k w[t+k,k] ds[t+k] for the previous tile: the
+//     filters w[t+k,.,k] come from MFMAs fed with z of token t+k (without
+//     SiLU the residual is folded into the tap-0 filter: ds = dy), ds[t+k]
+//     from the ds ring; a final step over the tokens after the chunk (zero
+//     past the sequence end) completes the chunk's last tile.
+// Where the x taps read for s stay in registers (see XR in the kernel), dw
+// comes before dx so that, with SiLU, they serve dw at once.
 // A second kernel adds the partials in a fixed order (deterministic).
 #pragma once
 #include <type_traits>
@@ -429,7 +431,7 @@ constexpr int lr_bwd_min_waves() {
     return (GPV == 8 && W == 8) || (VL && GPV == 8 && W == 7) ? 1
            : (GPV == 8 && W >= 5) || (GPV == 4 && W >= 7) ? 2
                                                           : 3;
-  else return GPV == 4 && W >= 7 ? 2 : 3;
+  else return (GPV == 4 && W >= 7) || (GPV == 2 && W == 8) ? 2 : 3;
 }
 
 // Packed rows (VL): a 32-entry ring of document positions beside the z ring;
@@ -455,6 +457,10 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
   constexpr int XP = Bg::XP, DP = Bg::DP, SP = Bg::SP, ZP = Bg::ZP, VPR = Bg::VPR, RPP = Bg::RPP,
                 NPASS = Bg::NPASS;
   constexpr int PF = 1;  // loads one step ahead: a step outlasts the load latency
+  // With SiLU the x taps read for the recomputation of s stay in registers for
+  // dw, where the instance keeps its occupancy without spilling (W <= 4, fewer
+  // than 8 groups per vector); the others read them from the ring again.
+  constexpr bool XR = W <= 4 && GPV < 8;
   const bool ACT = act != 0;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char *xring = smem + Bg::o_x, *dring = smem + Bg::o_ds, *dxstage = smem + Bg::o_dx,
@@ -684,6 +690,8 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
 #pragma unroll
         for (int e = 0; e < 4; ++e) ds[u][4 * h + e] = d4[e];
       }
+    // x taps of the lane's token (x[tau - k]), for dw
+    float xr[W][NU][V];
     if (ACT) {
       typename WFrag<BF>::T bz[KS];
       zfrag(tau, bz);
@@ -711,6 +719,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int i = 4 * h + e, m = u * GPV + i / Gm::H;
+              if constexpr (XR) xr[k][u][i] = x4[e];
               sacc[i] = fmaf(wacc[k][m >> 2][m & 3], x4[e], sacc[i]);
             }
           }
@@ -724,37 +733,41 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
           dslot(tau, u)[h] = f32x4{ds[u][4 * h], ds[u][4 * h + 1], ds[u][4 * h + 2], ds[u][4 * h + 3]};
       }
     }
-    __builtin_amdgcn_wave_barrier();
     // dx of the previous tile: dx[t'] = rho dy[t'] + sum_k w[t'+k,.,k] ds[t'+k]
-    if (st > 0 && do_dx) {
-      const int tp = t - 16 + j;
+    // (the wave barrier makes this wave's ds rows of the step visible)
+    auto dx_part = [&]() {
+      __builtin_amdgcn_wave_barrier();
+      if (st > 0 && do_dx) {
+        const int tp = t - 16 + j;
 #pragma unroll
-      for (int k = 0; k < W; ++k) {
-        typename WFrag<BF>::T bzs[KS];
-        zfrag(tp + k, bzs);
-        f32x4 wk[NP];
-        gen_tap_init<E, W, GPV, RB>(aw[k], bzs, wk, k == 0 ? rho_tap : 0.f);
-        if (VL && k > 0 && k > pring[(tp + k) & 31])
+        for (int k = 0; k < W; ++k) {
+          typename WFrag<BF>::T bzs[KS];
+          zfrag(tp + k, bzs);
+          f32x4 wk[NP];
+          gen_tap_init<E, W, GPV, RB>(aw[k], bzs, wk, k == 0 ? rho_tap : 0.f);
+          if (VL && k > 0 && k > pring[(tp + k) & 31])
 #pragma unroll
-          for (int p = 0; p < NP; ++p) wk[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int p = 0; p < NP; ++p) wk[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const f32x4 *src = dslot(tp + k, u);
+          for (int u = 0; u < NU; ++u) {
+            const f32x4 *src = dslot(tp + k, u);
 #pragma unroll
-          for (int h = 0; h < V / 4; ++h) {
-            const f32x4 d4 = src[h];
+            for (int h = 0; h < V / 4; ++h) {
+              const f32x4 d4 = src[h];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * h + e, m = u * GPV + i / Gm::H;
-              dxa[u][i] = fmaf(wk[m >> 2][m & 3], d4[e], dxa[u][i]);
+              for (int e = 0; e < 4; ++e) {
+                const int i = 4 * h + e, m = u * GPV + i / Gm::H;
+                dxa[u][i] = fmaf(wk[m >> 2][m & 3], d4[e], dxa[u][i]);
+              }
             }
           }
         }
-      }
 #pragma unroll
-      for (int u = 0; u < NU; ++u)
-        *reinterpret_cast<uint4 *>(dxstage + j * SP + (lcol + (u * 4 + q) * V) * RS) = pack<E>(dxa[u]);
-    }
+        for (int u = 0; u < NU; ++u)
+          *reinterpret_cast<uint4 *>(dxstage + j * SP + (lcol + (u * 4 + q) * V) * RS) = pack<E>(dxa[u]);
+      }
+    };
+    if constexpr (!XR) dx_part();
     if constexpr (!halo) {
       // filter-gradient slots; a chunk ends inside a tile only at the sequence
       // end, where ds is zero, so no lane needs masking
@@ -765,11 +778,16 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
 #pragma unroll
         for (int k = 0; k < W; ++k) {
           float xk[V];
+          if (XR && ACT) {
 #pragma unroll
-          for (int h = 0; h < V / 4; ++h) {
-            const f32x4 x4 = xslot(tau - k, u)[h];
+            for (int i = 0; i < V; ++i) xk[i] = xr[k][u][i];
+          } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) xk[4 * h + e] = x4[e];
+            for (int h = 0; h < V / 4; ++h) {
+              const f32x4 x4 = xslot(tau - k, u)[h];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) xk[4 * h + e] = x4[e];
+            }
           }
 #pragma unroll
           for (int gi = 0; gi < GPV; ++gi) {
@@ -844,6 +862,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
         }
       }
     }
+    if constexpr (XR) dx_part();
     __syncthreads();  // (2) dx staging and dz partials complete; ring reads done
   };
   issue(0, 0);
