@@ -272,6 +272,11 @@ COUNTER_RUNS = {
     "mlp_rnn_counters": ("SQ counters of the MLP (head-wise H=64, B=4 T=4096 D=8192, W in "
                          "2,3,4,8) and linear-RNN (low-rank R=16 H=8 SiLU, B=16 T=4096 D=4608) "
                          "configurations", "python3 bench.py --other-configs"),
+    "tied8_forward_counters": ("SQ counters of the linear-RNN forward (low-rank R=16 H=8 SiLU, "
+                               "B=16 T=4096 D=4608 W=4) on the vector-ALU kernel "
+                               "(lr_fwd_valu_kernel) and the matrix-core kernel (lr_fwd_kernel, "
+                               "libdsc_yard.so)",
+                               "python3 bench.py --tied8-forward --profile-ops 3"),
 }
 
 
@@ -338,6 +343,9 @@ TRACES = {
     "mlp_rnn_kernels": ("Kernels of the MLP (head-wise H=64, B=4 T=4096 D=8192, W in 2,3,4,8) "
                         "and linear-RNN (low-rank R=16 H=8 SiLU, B=16 T=4096 D=4608) "
                         "configurations", "python3 bench.py --other-configs"),
+    "tied8_forward_kernels": ("Kernels of the linear-RNN forward comparison (low-rank R=16 H=8 "
+                              "SiLU, B=16 T=4096 D=4608 W=4): vector-ALU and matrix-core kernels",
+                              "python3 bench.py --tied8-forward"),
     "generated_filter_kernels": ("Kernels of the generated-filter comparison, B=8 T=2048 "
                                  "D=6144 Dh=2048 W=4 H=16 bf16 residual: the fused kernel, "
                                  "then the library GEMM writing w and the head-wise forward",
@@ -401,6 +409,71 @@ def other_configs(dsc, di, torch, reps=10):
     for v in out.values():
         v["frac_of_peak"] = round(v["gbps"] / HBM_PEAK_GBPS, 4)
     return out
+
+
+def tied8_forward(dsc, di, torch, reps=10, rounds=5, profile_calls=0):
+    """The linear-RNN forward (low-rank R=16 tied over H=8 channels, W=4,
+    SiLU, bf16, B=16 T=4096 D=4608) on both kernels that can serve it:
+    libdsc.so's vector-ALU kernel and the matrix-core kernel kept in
+    libdsc_yard.so.  Both read the same two alternating input sets (x is
+    604 MB, beyond the last-level cache) in `rounds` interleaved rounds of
+    `reps` event-timed launches; the median launch of each.  With
+    profile_calls, only that many untimed launches of each (counter runs)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "dynamic_short_causal_amd", "libdsc_yard.so"))
+    lib.dsc_yard_lowrank_fwd_mfma.argtypes = ([ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3
+                                              + [ctypes.c_int] * 3 + [ctypes.c_void_p])
+    wl = di.WORKLOADS["rnn_lowrank_silu"]
+    inp = di.make(wl, need_dy=False)
+    sets = [(inp["x"].cuda(), inp["z"].cuda()) for _ in range(2)]
+    U = inp["U"].cuda()
+    del inp
+    ya, yb = torch.empty_like(sets[0][0]), torch.empty_like(sets[0][0])
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def valu(i):
+        x, z = sets[i % 2]
+        dsc.dsc_lowrank_fwd(x, z, U, ya, wl.W, wl.H, wl.residual, wl.act, stream)
+
+    def mfma(i):
+        x, z = sets[i % 2]
+        r = lib.dsc_yard_lowrank_fwd_mfma(P(x), P(z), P(U), P(yb), wl.B, wl.T, wl.D, wl.R,
+                                          int(wl.residual), int(wl.act), sp)
+        assert r == 0, r
+
+    if profile_calls:
+        for i in range(profile_calls):
+            valu(i)
+            mfma(i)
+        torch.cuda.synchronize()
+        return None
+    valu(0)
+    mfma(0)
+    torch.cuda.synchronize()
+    diff = float((ya.float() - yb.float()).abs().max() / yb.float().abs().max())
+    times = {"valu": [], "mfma": []}
+    for r in range(rounds):
+        for name, fn in (("valu", valu), ("mfma", mfma)):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for i, (a, b) in enumerate(ev):
+                a.record(stream)
+                fn(i + r)
+                b.record(stream)
+            torch.cuda.synchronize()
+            times[name] += [a.elapsed_time(b) * 1e3 for a, b in ev]
+    med = {k: sorted(v)[len(v) // 2] for k, v in times.items()}
+    N = wl.B * wl.T
+    nb = 2 * (2 * N * wl.D + N * wl.R) + 2 * wl.R * (wl.D // wl.H) * wl.W
+    return {"workload": "rnn_lowrank_silu forward (B=16 T=4096 D=4608 W=4 R=16 H=8, SiLU)",
+            "vector_alu_us": round(med["valu"], 1), "matrix_core_us": round(med["mfma"], 1),
+            "vector_alu_over_matrix_core": round(med["valu"] / med["mfma"], 4),
+            "vector_alu_frac_of_peak": round(nb / (med["valu"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "matrix_core_frac_of_peak": round(nb / (med["mfma"] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                              4),
+            "max_rel_diff": diff}
 
 
 def static_bench(dsc, di, torch, dev, steps, per_kernel_ms):
@@ -803,6 +876,10 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar=("NAME", "DIR"),
                     help="SQ counter passes under DIR... into profiles/NAME.md; NAME is one of "
                          + ", ".join(COUNTER_RUNS))
+    ap.add_argument("--tied8-forward", action="store_true",
+                    help="time the linear-RNN forward on the vector-ALU kernel and on the "
+                         "matrix-core kernel of libdsc_yard.so; with --profile-ops, run each "
+                         "that many times untimed (counter runs)")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the streaming ceilings of the step's read/write mixes")
     ap.add_argument("--summarize-gen-profiles", metavar="DIR",
@@ -841,6 +918,13 @@ def main():
         return
     if args.ceilings:
         print(json.dumps({"stream_ceilings": stream_ceilings(torch, dev)}), flush=True)
+        return
+    if args.tied8_forward:
+        r = tied8_forward(dsc, di, torch, profile_calls=args.profile_ops)
+        if r is None:
+            print("bench: profile passes done", file=sys.stderr, flush=True)
+        else:
+            print(json.dumps({"tied8_forward": r}), flush=True)
         return
     if args.generated_filters:
         if args.profile_ops:

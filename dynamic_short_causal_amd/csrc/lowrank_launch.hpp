@@ -3,13 +3,16 @@
 // lowrank_{fwd,bwd}_{bf16,f32}.hip so the four parts compile in parallel.
 // ---------------------------------------------------------------------------
 #pragma once
+#include <type_traits>
 #include "lowrank_impl.hpp"
 #include "lowrank_bwd_cl.hpp"
+#include "lowrank_fwd_valu.hpp"
 
 namespace dsc {
 
+// the matrix-core forward (lr_fwd_kernel)
 template <typename E, int W, int GPV, bool ACT, bool VL, int RB>
-static hipError_t launch_lr_fwd(const LrArgs &a) {
+static hipError_t launch_lr_fwd_mfma(const LrArgs &a) {
   using Gm = LrGeo<E, W, GPV>;
   hipStream_t s = (hipStream_t)a.stream;
   const float rho = a.residual ? 1.f : 0.f;
@@ -24,6 +27,15 @@ static hipError_t launch_lr_fwd(const LrArgs &a) {
                      (const E *)a.U, a.pos, (E *)a.y, (int)a.T, (int)a.D, a.R, TC, nchunk, ncb,
                      rho);
   return hipGetLastError();
+}
+
+template <typename E, int W, int GPV, bool ACT, bool VL, int RB>
+static hipError_t launch_lr_fwd(const LrArgs &a) {
+  // bf16 filters tied over 8 channels (one group per vector): vector ALUs
+  if constexpr (std::is_same_v<E, bf16> && GPV == 1 && RB == 1 && W <= 4) {
+    if (lr_fwd_uses_valu(a.bf16, a.D, a.W, a.H, a.R)) return launch_lr_fwd_valu<W, ACT, VL>(a);
+  }
+  return launch_lr_fwd_mfma<E, W, GPV, ACT, VL, RB>(a);
 }
 
 template <typename E>

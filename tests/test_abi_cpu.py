@@ -316,3 +316,29 @@ def test_noalloc_checks(lib):
     assert lib.dsc_lowrank_bwd_workspace_bytes(B, T, D, 4, 1, 16, 1) > d.NOALLOC_SCRATCH_BYTES
     assert call(B=B, T=T, D=D) == WS
     assert b"library buffer" in lib.dsc_last_error()
+
+
+def test_yardstick_library_checks():
+    """libdsc_yard.so (the matrix-core forward the benchmark times beside the
+    vector-ALU kernel for filters tied over 8 channels) loads, exports its one
+    call, and refuses arguments outside its case before touching a device."""
+    path = os.path.join(ROOT, "dynamic_short_causal_amd", "libdsc_yard.so")
+    if not os.path.exists(path):
+        import __graft_entry__ as ge
+        ge._library_builder().build()
+    y = ctypes.CDLL(path)
+    f = y.dsc_yard_lowrank_fwd_mfma
+    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_int] * 3 + [
+        ctypes.c_void_p]
+    p = ctypes.c_void_p
+    ok = dict(x=A, z=A + BIG, U=A + 2 * BIG, y=A + 3 * BIG, B=1, T=8, D=64, R=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(p(a["x"]), p(a["z"]), p(a["U"]), p(a["y"]), a["B"], a["T"], a["D"], a["R"], 1,
+                 1, None)
+    assert call(x=0) == -1
+    assert call(R=17) == -1
+    assert call(R=0) == -1
+    assert call(D=60) == -1
+    assert call(B=-1) == -1

@@ -183,3 +183,15 @@ def test_slot_counts_not_multiple_of_four(dsc, orc, W, H, dt):
     """Shapes whose per-lane filter-slot count leaves a partial dU MFMA block."""
     dtype = torch.bfloat16 if dt == "bf16" else torch.float32
     run_case(dsc, orc, 2, 40, 512, W, H, 16, dtype, True, True, 8300 + 10 * W + H)
+
+
+@pytest.mark.parametrize("W,R,T,residual,act", [
+    (1, 16, 70, True, False), (2, 8, 70, False, True), (3, 12, 33, True, True),
+    (4, 2, 70, True, True), (4, 16, 1, True, True), (3, 16, 2, False, False),
+    (4, 5, 70, True, True), (2, 16, 129, True, False)])
+def test_tied_eight_vector_alu_forward(dsc, orc, W, R, T, residual, act):
+    """bf16 filters tied over 8 channels form their taps on the vector ALUs
+    when W <= 4 and R is even (R = 5 takes the matrix-core kernel).  D = 576
+    is 72 channel vectors: one wave and a part-filled second per row."""
+    run_case(dsc, orc, 2, T, 576, W, 8, R, torch.bfloat16, residual, act,
+             8400 + 10 * W + R + T)

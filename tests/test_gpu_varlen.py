@@ -105,6 +105,13 @@ def test_lowrank_many_ranks(dsc, orc, R, W, H, dtype):
             packing(2, 97, 40 + R, 6))
 
 
+@pytest.mark.parametrize("W", [1, 2, 3])
+def test_lowrank_tied_eight_widths(dsc, orc, W):
+    """H = 8 in bf16 with W <= 4: the vector-ALU forward drops masked taps."""
+    lr_case(dsc, orc, 2, 97, 576, W, 8, 16, torch.bfloat16, True, True, 9350 + W,
+            packing(2, 97, 50 + W, 6))
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 5, 8])
 def test_lowrank_widths_silu(dsc, orc, W):
     lr_case(dsc, orc, 2, 97, 256, W, 1, 16, torch.bfloat16, True, True, 9300 + W,
