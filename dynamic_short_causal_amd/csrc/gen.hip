@@ -30,7 +30,8 @@
 //   * Epilogue: the tile is rounded to bf16 (the precision a stored w would
 //     have) into LDS; each thread then owns one 16-byte channel vector and a
 //     run of consecutive tokens, keeping the causal window in registers with
-//     8 rows of x in flight, and stores y in 16-byte non-temporal writes.  A
+//     the next 8 rows of x loaded while the current 8 are used (window slots
+//     instead of shifts), and stores y in 16-byte non-temporal writes.  A
 //     token tile may span sequences; the window restarts at every sequence
 //     start.
 // Token rows past the end and filter columns past G*W are read clamped to the
@@ -51,7 +52,7 @@ constexpr int kGT = 128;                   // tokens per workgroup
 constexpr int kGK = 32;                    // K-tile
 constexpr int kStages = 3;                 // LDS ring depth
 constexpr int kABytes = kGT * kGK * 2;     // A tile: 128 rows of 64 bytes
-constexpr int kUN = 8;                     // x rows in flight per thread (epilogue)
+constexpr int kUN = 8;                     // x rows per group in the epilogue (a multiple of W)
 
 template <int NC> struct GenTile {
   static_assert(NC == 128 || NC == 192 || NC == 256, "column tile");
@@ -193,22 +194,6 @@ __host__ __device__ __forceinline__ int gen_nseg(int nv, int threads, int minseg
   return nseg;
 }
 
-// Output of one token from its causal window win[k] = x_{t-k} and its taps.
-template <int W, bool ACT>
-__device__ __forceinline__ uint4 gen_conv_out(const float (&win)[W][8], const float (&taps)[W],
-                                              float rho) {
-  float o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < W; ++k) s = fmaf(taps[k], win[k][i], s);
-    if constexpr (ACT) s = silu_f(s);
-    o[i] = fmaf(rho, win[0][i], s);
-  }
-  return pack<bf16>(o);
-}
-
 // ---------------------------------------------------------------------------
 // The kernel: GEMM of the tile, then its convolution, by all 4 waves.
 // ---------------------------------------------------------------------------
@@ -218,6 +203,7 @@ __global__ __launch_bounds__(kGenThreads, 2) void gen_fwd_kernel(
     bf16 *__restrict__ y, int64_t N, int T, int D, int Dh, int H, int GW, int ncb, int ntt,
     int ngrp, float rho) {
   using Tl = GenTile<NC>;
+  static_assert(kUN % W == 0, "window slots repeat every W tokens of a group");
   constexpr int GB = NC / W;  // groups per workgroup
   __shared__ __align__(16) unsigned char smem[Tl::Lds];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -255,46 +241,63 @@ __global__ __launch_bounds__(kGenThreads, 2) void gen_fwd_kernel(
     const int tl0 = sgi * seg;
     if (n0 + tl0 >= N) continue;
     int t = (int)((n0 + tl0) % T);
+    // rows of the segment; loads past its last row repeat that row (cache
+    // hits), so every load is unconditional and a group of kUN rows can be in
+    // flight while the previous one is used
+    const int64_t nlast = min(N, n0 + tl0 + seg) - 1;
+    auto xrow = [&](int64_t n) { return ld16nt(x + min(n, nlast) * D + c); };
+    // window slots: slot u % W holds the token at offset u of a group (kUN is
+    // a multiple of W), the slots before the first group hold the W-1 tokens
+    // before the segment (zero before a sequence start)
     float win[W][8];
-    // the window before the segment's first token (same sequence only)
 #pragma unroll
     for (int k = 1; k < W; ++k) {
+      const int sl = (W - k) % W;
       if (t - k >= 0) {
-        unpack<bf16>(ld16(x + (n0 + tl0 - k) * D + c), win[k - 1]);
+        unpack<bf16>(ld16(x + (n0 + tl0 - k) * D + c), win[sl]);
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) win[k - 1][i] = 0.f;
+        for (int i = 0; i < 8; ++i) win[sl][i] = 0.f;
       }
     }
+    uint4 xc[kUN];
+#pragma unroll
+    for (int u = 0; u < kUN; ++u) xc[u] = xrow(n0 + tl0 + u);
     for (int tl = tl0; tl < tl0 + seg; tl += kUN) {
-      uint4 xr[kUN];
+      uint4 xn[kUN];
+#pragma unroll
+      for (int u = 0; u < kUN; ++u) xn[u] = xrow(n0 + tl + kUN + u);
 #pragma unroll
       for (int u = 0; u < kUN; ++u) {
         const int64_t n = n0 + tl + u;
-        xr[u] = n < N ? ld16nt(x + n * D + c) : make_uint4(0u, 0u, 0u, 0u);
-      }
+        if (n <= nlast) {
+          const int sl = u % W;
+          if (t == 0) {  // a sequence starts: nothing before it
 #pragma unroll
-      for (int u = 0; u < kUN; ++u) {
-        const int64_t n = n0 + tl + u;
-        if (n >= N) break;
-        if (t == 0) {  // a sequence starts: nothing before it
+            for (int k = 0; k < W; ++k)
 #pragma unroll
-          for (int k = 0; k < W; ++k)
+              for (int i = 0; i < 8; ++i) win[k][i] = 0.f;
+          }
+          unpack<bf16>(xc[u], win[sl]);
+          float taps[W];
+          unpack_row<bf16, W>(
+              ld_row<bf16, W>(reinterpret_cast<const bf16 *>(smem + (tl + u) * Tl::WP) + gl * W),
+              taps);
+          float o[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) win[k][i] = 0.f;
+          for (int i = 0; i < 8; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int k = 0; k < W; ++k) s = fmaf(taps[k], win[(sl - k + W) % W][i], s);
+            if constexpr (ACT) s = silu_f(s);
+            o[i] = fmaf(rho, win[sl][i], s);
+          }
+          st16nt(y + n * D + c, pack<bf16>(o));
+          if (++t == T) t = 0;
         }
-#pragma unroll
-        for (int k = W - 1; k > 0; --k)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) win[k][i] = win[k - 1][i];
-        unpack<bf16>(xr[u], win[0]);
-        float taps[W];
-        unpack_row<bf16, W>(
-            ld_row<bf16, W>(reinterpret_cast<const bf16 *>(smem + (tl + u) * Tl::WP) + gl * W),
-            taps);
-        st16nt(y + n * D + c, gen_conv_out<W, ACT>(win, taps, rho));
-        if (++t == T) t = 0;
       }
+#pragma unroll
+      for (int u = 0; u < kUN; ++u) xc[u] = xn[u];
     }
   }
 }
