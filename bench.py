@@ -112,11 +112,26 @@ def cpu_baseline(target_s=12.0):
         orc.lowrank_bwd(x, z, U, dy, W, 1, residual=True)
         el += time.perf_counter() - t0
         done += 1
-    return {"value": round(done * T / el, 1), "unit": "tokens/s", "cores": orc.num_threads(),
+    cores = orc.num_threads()
+    # the same oracle on one thread, over the first sequence
+    orc.set_num_threads(1)
+    try:
+        x, dy, w, z, U = seq(0)
+        t0 = time.perf_counter()
+        orc.headwise_fwd(x, w, Hh, residual=True)
+        orc.headwise_bwd(x, w, dy, Hh, residual=True)
+        orc.lowrank_fwd(x, z, U, W, 1, residual=True)
+        orc.lowrank_bwd(x, z, U, dy, W, 1, residual=True)
+        el1 = time.perf_counter() - t0
+    finally:
+        orc.set_num_threads(cores)
+    return {"value": round(done * T / el, 1), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{done} of the {B} sequences (T={T}, D={D}, W={W}; head-wise H={Hh} and "
                       f"low-rank R={R} H=1, residual, fwd+bwd), fp64 C oracle with OpenMP; "
-                      f"{el:.1f} s"}
+                      f"{el:.1f} s",
+            "one_thread": {"value": round(T / el1, 1), "unit": "tokens/s", "cores": 1,
+                           "sample": f"the first sequence on one thread; {el1:.1f} s"}}
 
 
 OP_KERNELS = {  # op -> kernel names (rocprofv3) that one call launches
@@ -1010,6 +1025,16 @@ def main():
     per_kernel_ms = {n: sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps))
                      / args.steps for i, n in enumerate(names)}
 
+    def pct(vals):
+        v = sorted(vals)
+        at = lambda f: v[min(len(v) - 1, int(f * (len(v) - 1) + 0.5))]
+        return {"p10": round(at(0.1), 4), "p50": round(at(0.5), 4), "p90": round(at(0.9), 4)}
+    # spread over the K timed steps: each op's event time, and their sum per step
+    spread = {n: pct([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)])
+              for i, n in enumerate(names)}
+    spread["step_sum_of_ops"] = pct([sum(ev[k][i][0].elapsed_time(ev[k][i][1])
+                                         for i in range(len(names))) for k in range(args.steps)])
+
     # Each op alone: blocks of 10 back-to-back calls between two events, the
     # calls alternating between two complete sets of the op's tensors (inputs,
     # outputs and workspace: more than the last-level cache holds, so neither
@@ -1071,6 +1096,12 @@ def main():
     gen = gen_bench(dsc, di, torch, dev, args.steps)
     print("bench: streaming ceilings", file=sys.stderr, flush=True)
     ceilings = stream_ceilings(torch, dev)
+    print("bench: timing the MLP and linear-RNN configurations", file=sys.stderr, flush=True)
+    others = other_configs(dsc, di, torch)
+    torch.cuda.empty_cache()
+    print("bench: timing the linear-RNN forward on both kernels", file=sys.stderr, flush=True)
+    tied8 = tied8_forward(dsc, di, torch)
+    torch.cuda.empty_cache()
 
     nbytes = algorithmic_bytes(B, T, D, W, Hh, R, Hl)
     ms_per_step = elapsed / args.steps * 1e3
@@ -1121,6 +1152,9 @@ def main():
         "packed_rows": varlen,
         "generated_filters": gen,
         "stream_ceilings": ceilings,
+        "spread_ms": spread,
+        "other_configs": others,
+        "tied8_forward": tied8,
         "roofline": {"bound": "hbm", "kernel": dom, "timing": "blocks of 10 back-to-back calls",
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
