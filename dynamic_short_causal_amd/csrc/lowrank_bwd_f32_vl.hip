@@ -1,5 +1,5 @@
 // lowrank_bwd_f32_vl.hip -- instantiates the low-rank bwd launchers for float (packed rows) with
-// DSC_LR_RB blocks of 16 ranks; the build compiles it once per block count.
+// DSC_LR_RB blocks of 16 ranks; build.py compiles it once per block count.
 #include "lowrank_launch.hpp"
 
 namespace dsc {
