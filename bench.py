@@ -125,8 +125,20 @@ def cpu_baseline(target_s=12.0):
         el1 = time.perf_counter() - t0
     finally:
         orc.set_num_threads(cores)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    per_token = sum(algorithmic_bytes(B, T, D, W, Hh, R, WORKLOAD["H_lowrank"]).values()) / (B * T)
     return {"value": round(done * T / el, 1), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
+            "gbps": round(per_token * done * T / el / 1e9, 3),
+            "cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{done} of the {B} sequences (T={T}, D={D}, W={W}; head-wise H={Hh} and "
                       f"low-rank R={R} H=1, residual, fwd+bwd), fp64 C oracle with OpenMP; "
                       f"{el:.1f} s",
