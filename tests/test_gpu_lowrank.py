@@ -116,17 +116,22 @@ def test_empty_batch_zeroes_dU(dsc, orc, B, T):
     assert torch.all(dU == 0)
 
 
-def test_deterministic(dsc, orc):
+@pytest.mark.parametrize("H,act", [(1, False), (8, True)])
+def test_deterministic(dsc, orc, H, act):
+    """Repeated calls give the same bits: per-channel filters (channel-per-lane
+    backward) and filters tied over 8 channels with SiLU (vector-ALU forward,
+    token-per-lane backward)."""
     x = di.randn((2, 300, 1024), 1.0, 8100, "bf16").to(gu.dev())
     z = di.randn((2, 300, 16), 1.0, 8102, "bf16").to(gu.dev())
-    U = di.randn((16, 1024 * 4), 0.125, 8103, "bf16").to(gu.dev())
+    U = di.randn((16, (1024 // H) * 4), 0.125, 8103, "bf16").to(gu.dev())
     dy = di.randn((2, 300, 1024), 1.0, 8104, "bf16").to(gu.dev())
-    a = dsc.lowrank_bwd(x, z, U, dy, 4, 1, True, False)
-    b = dsc.lowrank_bwd(x, z, U, dy, 4, 1, True, False)
+    a = dsc.lowrank_bwd(x, z, U, dy, 4, H, True, act)
+    b = dsc.lowrank_bwd(x, z, U, dy, 4, H, True, act)
     torch.cuda.synchronize()
     for p, q in zip(a, b):
         assert torch.equal(p, q)
-    assert torch.equal(dsc.lowrank_fwd(x, z, U, 4, 1, True), dsc.lowrank_fwd(x, z, U, 4, 1, True))
+    assert torch.equal(dsc.lowrank_fwd(x, z, U, 4, H, True, act),
+                       dsc.lowrank_fwd(x, z, U, 4, H, True, act))
 
 
 def test_lowrank_equals_headwise_on_gpu(dsc, orc):
