@@ -304,6 +304,11 @@ COUNTER_RUNS = {
                                "(lr_fwd_valu_kernel) and the matrix-core kernel (lr_fwd_kernel, "
                                "libdsc_yard.so)",
                                "python3 bench.py --tied8-forward --profile-ops 3"),
+    "tied8_backward_counters": ("SQ counters of the linear-RNN backward (low-rank R=16 H=8 "
+                                "SiLU, B=16 T=4096 D=4608 W=4) on the matrix-core kernel "
+                                "(lr_bwd_kernel) and the vector-ALU kernel (lr_bwd_valu_kernel, "
+                                "libdsc_yard.so), each with its reduction",
+                                "python3 bench.py --tied8-backward --profile-ops 3"),
 }
 
 
@@ -373,6 +378,10 @@ TRACES = {
     "tied8_forward_kernels": ("Kernels of the linear-RNN forward comparison (low-rank R=16 H=8 "
                               "SiLU, B=16 T=4096 D=4608 W=4): vector-ALU and matrix-core kernels",
                               "python3 bench.py --tied8-forward"),
+    "tied8_backward_kernels": ("Kernels of the linear-RNN backward comparison (low-rank R=16 "
+                               "H=8 SiLU, B=16 T=4096 D=4608 W=4): matrix-core and vector-ALU "
+                               "kernels, each with its reduction",
+                               "python3 bench.py --tied8-backward"),
     "generated_filter_kernels": ("Kernels of the generated-filter comparison, B=8 T=2048 "
                                  "D=6144 Dh=2048 W=4 H=16 bf16 residual: the fused kernel, "
                                  "then the library GEMM writing w and the head-wise forward",
@@ -500,6 +509,83 @@ def tied8_forward(dsc, di, torch, reps=10, rounds=5, profile_calls=0):
             "vector_alu_frac_of_peak": round(nb / (med["valu"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "matrix_core_frac_of_peak": round(nb / (med["mfma"] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                                               4),
+            "max_rel_diff": diff}
+
+
+def tied8_backward(dsc, di, torch, reps=10, rounds=5, profile_calls=0):
+    """The linear-RNN backward (low-rank R=16 tied over H=8 channels, W=4,
+    SiLU, bf16, B=16 T=4096 D=4608) on both kernels that can serve it:
+    libdsc.so's matrix-core backward and the vector-ALU backward kept in
+    libdsc_yard.so, each with its partial-sum reduction.  Two alternating
+    input sets (x and dy are 604 MB each), `rounds` interleaved rounds of
+    `reps` event-timed calls, the median call of each.  With profile_calls,
+    only that many untimed calls of each (counter runs)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "dynamic_short_causal_amd", "libdsc_yard.so"))
+    lib.dsc_yard_lowrank_bwd_valu.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int64] * 3
+                                              + [ctypes.c_int] * 3 + [ctypes.c_void_p])
+    lib.dsc_yard_lowrank_bwd_valu_workspace.restype = ctypes.c_size_t
+    lib.dsc_yard_lowrank_bwd_valu_workspace.argtypes = [ctypes.c_int64] * 3
+    wl = di.WORKLOADS["rnn_lowrank_silu"]
+    inp = di.make(wl)
+    sets = [(inp["x"].cuda(), inp["z"].cuda(), inp["dy"].cuda()) for _ in range(2)]
+    U = inp["U"].cuda()
+    del inp
+    x0, z0 = sets[0][0], sets[0][1]
+    outs = {k: (torch.empty_like(x0), torch.empty_like(z0), torch.empty_like(U))
+            for k in ("mfma", "valu")}
+    ws_m = dsc.lowrank_workspace(x0, z0, wl.W, wl.H)
+    ws_v = torch.empty(lib.dsc_yard_lowrank_bwd_valu_workspace(wl.B, wl.T, wl.D),
+                       dtype=torch.uint8, device=x0.device)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def mfma(i):
+        x, z, dy = sets[i % 2]
+        dx, dz, dU = outs["mfma"]
+        dsc.dsc_lowrank_bwd(x, z, U, dy, dx, dz, dU, ws_m, wl.W, wl.H, wl.residual, wl.act,
+                            stream)
+
+    def valu(i):
+        x, z, dy = sets[i % 2]
+        dx, dz, dU = outs["valu"]
+        r = lib.dsc_yard_lowrank_bwd_valu(P(x), P(z), P(U), P(dy), P(dx), P(dz), P(dU), P(ws_v),
+                                          wl.B, wl.T, wl.D, wl.R, int(wl.residual), int(wl.act),
+                                          sp)
+        assert r == 0, r
+
+    if profile_calls:
+        for i in range(profile_calls):
+            mfma(i)
+            valu(i)
+        torch.cuda.synchronize()
+        return None
+    mfma(0)
+    valu(0)
+    torch.cuda.synchronize()
+    diff = {n: float((a.float() - b.float()).abs().max() / a.float().abs().max())
+            for n, a, b in zip(("dx", "dz", "dU"), outs["mfma"], outs["valu"])}
+    times = {"mfma": [], "valu": []}
+    for r in range(rounds):
+        for name, fn in (("mfma", mfma), ("valu", valu)):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for i, (a, b) in enumerate(ev):
+                a.record(stream)
+                fn(i + r)
+                b.record(stream)
+            torch.cuda.synchronize()
+            times[name] += [a.elapsed_time(b) * 1e3 for a, b in ev]
+    med = {k: sorted(v)[len(v) // 2] for k, v in times.items()}
+    N = wl.B * wl.T
+    nb = 2 * (3 * N * wl.D + 2 * N * wl.R) + 2 * 2 * wl.R * (wl.D // wl.H) * wl.W
+    return {"workload": "rnn_lowrank_silu backward (B=16 T=4096 D=4608 W=4 R=16 H=8, SiLU)",
+            "matrix_core_us": round(med["mfma"], 1), "vector_alu_us": round(med["valu"], 1),
+            "vector_alu_over_matrix_core": round(med["valu"] / med["mfma"], 4),
+            "matrix_core_frac_of_peak": round(nb / (med["mfma"] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                              4),
+            "vector_alu_frac_of_peak": round(nb / (med["valu"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "max_rel_diff": diff}
 
 
@@ -907,6 +993,10 @@ def main():
                     help="time the linear-RNN forward on the vector-ALU kernel and on the "
                          "matrix-core kernel of libdsc_yard.so; with --profile-ops, run each "
                          "that many times untimed (counter runs)")
+    ap.add_argument("--tied8-backward", action="store_true",
+                    help="time the linear-RNN backward on the matrix-core kernel and on the "
+                         "vector-ALU kernel of libdsc_yard.so; with --profile-ops, run each "
+                         "that many times untimed (counter runs)")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the streaming ceilings of the step's read/write mixes")
     ap.add_argument("--summarize-gen-profiles", metavar="DIR",
@@ -945,6 +1035,13 @@ def main():
         return
     if args.ceilings:
         print(json.dumps({"stream_ceilings": stream_ceilings(torch, dev)}), flush=True)
+        return
+    if args.tied8_backward:
+        r = tied8_backward(dsc, di, torch, profile_calls=args.profile_ops)
+        if r is None:
+            print("bench: profile passes done", file=sys.stderr, flush=True)
+        else:
+            print(json.dumps({"tied8_backward": r}), flush=True)
         return
     if args.tied8_forward:
         r = tied8_forward(dsc, di, torch, profile_calls=args.profile_ops)
@@ -1114,6 +1211,9 @@ def main():
     print("bench: timing the linear-RNN forward on both kernels", file=sys.stderr, flush=True)
     tied8 = tied8_forward(dsc, di, torch)
     torch.cuda.empty_cache()
+    print("bench: timing the linear-RNN backward on both kernels", file=sys.stderr, flush=True)
+    tied8b = tied8_backward(dsc, di, torch)
+    torch.cuda.empty_cache()
 
     nbytes = algorithmic_bytes(B, T, D, W, Hh, R, Hl)
     ms_per_step = elapsed / args.steps * 1e3
@@ -1167,6 +1267,7 @@ def main():
         "spread_ms": spread,
         "other_configs": others,
         "tied8_forward": tied8,
+        "tied8_backward": tied8b,
         "roofline": {"bound": "hbm", "kernel": dom, "timing": "blocks of 10 back-to-back calls",
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -122,20 +122,21 @@ def build_stream_ceiling():
     return STREAM_LIB
 
 
-YARD_SRC = os.path.join(CSRC, "yard_lowrank_fwd_mfma.hip")
+YARD_SRC = os.path.join(CSRC, "yardstick.hip")
 YARD_LIB = os.path.join(PKG, "libdsc_yard.so")
 
 
 def build_yardstick():
-    """libdsc_yard.so: the matrix-core low-rank forward for filters tied over
-    8 channels, which the benchmark's --tied8-forward mode times beside the
-    vector-ALU kernel libdsc.so uses there (not part of libdsc.so)."""
+    """libdsc_yard.so: the other side of two kernel choices for filters tied
+    over 8 channels (the matrix-core forward, the vector-ALU backward), which
+    the benchmark's --tied8-forward and --tied8-backward modes time beside
+    the kernels libdsc.so uses there (not part of libdsc.so)."""
     tmp = YARD_LIB + ".tmp"
     cmd = [HIPCC, *[f for f in FLAGS if not f.startswith("-Rpass")], "-shared", "-I", CSRC,
            YARD_SRC, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for yard_lowrank_fwd_mfma.hip:\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for yardstick.hip:\n{r.stderr}")
     os.replace(tmp, YARD_LIB)
     return YARD_LIB
 

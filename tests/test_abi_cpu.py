@@ -342,3 +342,16 @@ def test_yardstick_library_checks():
     assert call(R=0) == -1
     assert call(D=60) == -1
     assert call(B=-1) == -1
+    # the vector-ALU backward yardstick: workspace query and argument checks
+    y.dsc_yard_lowrank_bwd_valu_workspace.restype = ctypes.c_size_t
+    y.dsc_yard_lowrank_bwd_valu_workspace.argtypes = [ctypes.c_int64] * 3
+    assert y.dsc_yard_lowrank_bwd_valu_workspace(2, 300, 1024) > 0
+    assert y.dsc_yard_lowrank_bwd_valu_workspace(2, 300, 1020) == 0
+    g = y.dsc_yard_lowrank_bwd_valu
+    g.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int64] * 3 + [ctypes.c_int] * 3 + [
+        ctypes.c_void_p]
+    ptrs = [p(A + i * BIG) for i in range(8)]
+    assert g(*([p(0)] + ptrs[1:]), 1, 8, 64, 16, 1, 1, None) == -1   # null x
+    assert g(*ptrs, 1, 8, 64, 15, 1, 1, None) == -1                  # odd R
+    assert g(*ptrs, 1, 8, 64, 18, 1, 1, None) == -1                  # R > 16
+    assert g(*ptrs, 1, 8, 60, 16, 1, 1, None) == -1                  # D not a multiple of 8
