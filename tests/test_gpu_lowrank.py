@@ -200,3 +200,39 @@ def test_tied_eight_vector_alu_forward(dsc, orc, W, R, T, residual, act):
     is 72 channel vectors: one wave and a part-filled second per row."""
     run_case(dsc, orc, 2, T, 576, W, 8, R, torch.bfloat16, residual, act,
              8400 + 10 * W + R + T)
+
+
+@pytest.mark.parametrize("T,act,residual", [(300, True, False), (70, False, True), (1, True, True)])
+def test_vector_alu_backward_yardstick(dsc, orc, T, act, residual):
+    """The vector-ALU backward kept in libdsc_yard.so (measured against the
+    library's matrix-core backward by the benchmark) matches the oracle at
+    the bar of the library's own kernels: bf16, W=4, H=8, R=16, D=576 (one
+    full and one part-filled wave per row)."""
+    import ctypes
+    import os
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(dsc.__file__), "libdsc_yard.so"))
+    lib.dsc_yard_lowrank_bwd_valu_workspace.restype = ctypes.c_size_t
+    lib.dsc_yard_lowrank_bwd_valu_workspace.argtypes = [ctypes.c_int64] * 3
+    lib.dsc_yard_lowrank_bwd_valu.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int64] * 3
+                                              + [ctypes.c_int] * 3 + [ctypes.c_void_p])
+    B, D, W, H, R, seed = 2, 576, 4, 8, 16, 8500 + T
+    gu.say(f"  case yardstick B={B} T={T} D={D} act={act} res={residual}")
+    x = di.randn((B, T, D), 1.0, seed, "bf16")
+    z = di.randn((B, T, R), 1.0, seed + 2, "bf16")
+    U = di.randn((R, (D // H) * W), (1.0 / (R * W)) ** 0.5 * 2, seed + 3, "bf16")
+    dy = di.randn((B, T, D), 1.0, seed + 4, "bf16")
+    xd, zd, Ud, dyd = (t.to(gu.dev()) for t in (x, z, U, dy))
+    dx, dz, dU = torch.empty_like(xd), torch.empty_like(zd), torch.empty_like(Ud)
+    ws = torch.empty(lib.dsc_yard_lowrank_bwd_valu_workspace(B, T, D), dtype=torch.uint8,
+                     device=gu.dev())
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    s = torch.cuda.current_stream()
+    assert lib.dsc_yard_lowrank_bwd_valu(P(xd), P(zd), P(Ud), P(dyd), P(dx), P(dz), P(dU), P(ws),
+                                         B, T, D, R, int(residual), int(act),
+                                         ctypes.c_void_p(s.cuda_stream)) == 0
+    torch.cuda.synchronize()
+    X, Z, UU, DY = gu.f64(x), gu.f64(z), gu.f64(U), gu.f64(dy)
+    dxo, dzo, dUo = orc.lowrank_bwd(X, Z, UU, DY, W, H, residual, act)
+    gu.check("dx", dx, dxo, torch.bfloat16, "dx")
+    gu.check("dz", dz, dzo, torch.bfloat16, "dz")
+    gu.check("dU", dU, dUo, torch.bfloat16, "dU")
