@@ -99,6 +99,36 @@ __device__ __forceinline__ uint4 sel4(bool ok, uint4 v) {
   return ok ? v : make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Byte offset of channel vector vi (0..15; wave vi / 4, lane quarter vi % 4)
+// in an fp32 ring row.  gfx950's LDS has 64 four-byte banks and serves a
+// 16-byte read 16 lanes per pass; measured with a probe, a pass holds the
+// lanes of one half-wave with equal parity of lane bits 2..4.  A ring read
+// has lane (q, j) on row j + c and vector 4w + q, so a pass holds quarters q
+// and q ^ 1 on complementary sets of 8 rows: placing those two vectors 256
+// bytes (one turn of the banks) apart puts the pass on 16 distinct 4-bank
+// windows, where the plain order put two lanes on one window.  bf16 rows only
+// (16 vectors of 8 fp32, 512 bytes); fp32 rows (16 vectors of 16 bytes) keep
+// the plain order, which would need twice the row to pair them.
+template <typename E> __device__ __forceinline__ int ring_vec(int vi) {
+  if constexpr (sizeof(E) == 2) return (2 * (vi >> 2) + ((vi & 3) >> 1)) * 32 + (vi & 1) * 256;
+  else return vi * 16;
+}
+// Vector vv of a ring row from its V fp32 values.  For bf16 the two 16-byte
+// halves go out in the opposite order on odd vectors, so that each of the
+// two writes by 16 consecutive vectors covers 16 distinct 4-bank windows.
+template <typename E>
+__device__ __forceinline__ void ring_store(unsigned char *row, int vv, const float (&v)[Vw<E>::n]) {
+  f32x4 *dst = reinterpret_cast<f32x4 *>(row + ring_vec<E>(vv));
+  if constexpr (Vw<E>::n == 8) {
+    const bool odd = vv & 1;
+    const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+    dst[odd ? 1 : 0] = odd ? b : a;
+    dst[odd ? 0 : 1] = odd ? a : b;
+  } else {
+    dst[0] = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
 // Filter slot sigma = k*NG + m of lane quarter qq; m = u*GPV + gi names vector
 // u*4 + qq of the wave slice and group gi inside it.  Returns the U column,
 // or -1 when the channel lies beyond D.
@@ -242,17 +272,15 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
   const int cc = cb * Gm::CB + vv * V;
   const bool cc_ok = cc < D;
   // ring row slot of token `tok` (any sign): tok & 31 is tok mod 32
+  static_assert(Gm::CB == 16 * V && NU == 1, "16 channel vectors per ring row");
   auto ring_put = [&](int tok, const uint4 &raw, bool ok) {
     float v[V];
     unpack<E>(sel4(ok, raw), v);
-    f32x4 *dst = reinterpret_cast<f32x4 *>(ring + (tok & 31) * XR + vv * V * 4);
-#pragma unroll
-    for (int h = 0; h < V / 4; ++h) dst[h] = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+    ring_store<E>(ring + (tok & 31) * XR, vv, v);
   };
   // the V channels of lane vector u at token `tok`, as V/4 16-byte pieces
   auto xrow = [&](int tok, int u) {
-    return reinterpret_cast<const f32x4 *>(ring + (tok & 31) * XR +
-                                           (wave * Gm::CW + (u * 4 + q) * V) * 4);
+    return reinterpret_cast<const f32x4 *>(ring + (tok & 31) * XR + ring_vec<E>(wave * 4 + u * 4 + q));
   };
 
   typename WFrag<Gm::BF>::T aw[W][NP][KS];
@@ -488,11 +516,12 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) voff[p] = cbase + (uint32_t)((p * RPP + rr) * D * RS);
   const int lcol = wave * Gm::CW;
+  static_assert(Gm::CB == 16 * V && NU == 1, "16 channel vectors per ring row");
   auto xslot = [&](int tok, int u) {
-    return reinterpret_cast<const f32x4 *>(xring + (tok & 31) * XP + (lcol + (u * 4 + q) * V) * 4);
+    return reinterpret_cast<const f32x4 *>(xring + (tok & 31) * XP + ring_vec<E>(wave * 4 + u * 4 + q));
   };
   auto dslot = [&](int tok, int u) {
-    return reinterpret_cast<f32x4 *>(dring + (tok & 31) * DP + (lcol + (u * 4 + q) * V) * 4);
+    return reinterpret_cast<f32x4 *>(dring + (tok & 31) * DP + ring_vec<E>(wave * 4 + u * 4 + q));
   };
   auto zrow = [&](int tok) { return reinterpret_cast<const E *>(zring + (tok & 31) * ZP); };
   auto zfrag = [&](int tok, typename WFrag<BF>::T (&f)[KS]) {
@@ -568,9 +597,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
       const uint4 raw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff[p], 0, 0));
       float v[V];
       unpack<E>(raw, v);
-      f32x4 *dst = reinterpret_cast<f32x4 *>(xring + ((tb + p * RPP + rr) & 31) * XP + vv * V * 4);
-#pragma unroll
-      for (int h = 0; h < V / 4; ++h) dst[h] = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+      ring_store<E>(xring + ((tb + p * RPP + rr) & 31) * XP, vv, v);
     }
     const brsrc rz = zslab(tb, tb < 0 ? tb : T);
 #pragma unroll
@@ -617,15 +644,11 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
       const int row = (t + p * RPP + rr) & 31;
       float v[V];
       unpack<E>(dyn[sl][p], v);
-      f32x4 *dd = reinterpret_cast<f32x4 *>(dring + row * DP + vv * V * 4);
-#pragma unroll
-      for (int h = 0; h < V / 4; ++h) dd[h] = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+      ring_store<E>(dring + row * DP, vv, v);
       if (ACT || !halo) {
         float w[V];
         unpack<E>(xn[sl][p], w);
-        f32x4 *xd = reinterpret_cast<f32x4 *>(xring + row * XP + vv * V * 4);
-#pragma unroll
-        for (int h = 0; h < V / 4; ++h) xd[h] = f32x4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
+        ring_store<E>(xring + row * XP, vv, w);
       }
     }
 #pragma unroll
