@@ -950,4 +950,61 @@ __global__ __launch_bounds__(256) void lr_reduce_kernel(const float *__restrict_
     }
   }
 }
+
+// The same sums, four consecutive outputs per thread with 16-byte loads of
+// the partials (R and G*W multiples of 4, so that four consecutive outputs
+// share a token row of dz or a rank row of dU).  Same order of addition per
+// output, so the same bits.
+template <typename E>
+__global__ __launch_bounds__(256) void lr_reduce4_kernel(const float *__restrict__ dzp,
+                                                          const float *__restrict__ dUp,
+                                                          E *__restrict__ dz, E *__restrict__ dU,
+                                                          int64_t N, int R, int RP, int ncb,
+                                                          int64_t GW, int nparts) {
+  const int64_t nz = N * R / 4, nu = (int64_t)R * GW / 4;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nz + nu;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const float *src;
+    int64_t stride;
+    int cnt;
+    if (idx < nz) {
+      const int64_t e = idx * 4, n = e / R;
+      const int r = (int)(e - n * R);
+      src = dzp + n * RP + r; stride = N * RP; cnt = ncb;
+    } else {
+      const int64_t o = (idx - nz) * 4;
+      const int64_t r = o / GW, col = o - r * GW;
+      src = dUp + r * GW + col; stride = (int64_t)RP * GW; cnt = nparts;
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int c = 0;
+    for (; c + 8 <= cnt; c += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const f32x4 *>(src + (c + i) * stride);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc[0] += v[i][0];
+        acc[1] += v[i][1];
+        acc[2] += v[i][2];
+        acc[3] += v[i][3];
+      }
+    }
+    for (; c < cnt; ++c) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(src + c * stride);
+      acc[0] += v[0];
+      acc[1] += v[1];
+      acc[2] += v[2];
+      acc[3] += v[3];
+    }
+    if constexpr (sizeof(E) == 2) {
+      const uint2 b = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      if (idx < nz) *reinterpret_cast<uint2 *>(dz + idx * 4) = b;
+      else *reinterpret_cast<uint2 *>(dU + (idx - nz) * 4) = b;
+    } else {
+      if (idx < nz) *reinterpret_cast<f32x4 *>(dz + idx * 4) = acc;
+      else *reinterpret_cast<f32x4 *>(dU + (idx - nz) * 4) = acc;
+    }
+  }
+}
 }  // namespace dsc

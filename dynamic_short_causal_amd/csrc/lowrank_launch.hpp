@@ -101,13 +101,20 @@ static hipError_t launch_lr_reduce(const LrArgs &a, const LrBwdPlan &p, const fl
   hipStream_t s = (hipStream_t)a.stream;
   const int64_t N = a.B * a.T;
   const int64_t GW = (a.D / a.H) * a.W;
-  const int64_t total = N * a.R + (int64_t)a.R * GW;
+  // four outputs per thread where R and G*W allow it (16-byte partial loads)
+  const bool by4 = a.R % 4 == 0 && GW % 4 == 0;
+  const int64_t total = (N * a.R + (int64_t)a.R * GW) / (by4 ? 4 : 1);
   int64_t grid = (total + 255) / 256;
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((lr_reduce_kernel<E>), dim3((unsigned)grid), dim3(256), 0, s, dzp, dUp,
-                     (E *)a.dz, (E *)a.dU, N, a.R, (int)p.rpad, (int)p.ncb, GW,
-                     (int)(a.B * p.nchunk));
+  if (by4)
+    hipLaunchKernelGGL((lr_reduce4_kernel<E>), dim3((unsigned)grid), dim3(256), 0, s, dzp, dUp,
+                       (E *)a.dz, (E *)a.dU, N, a.R, (int)p.rpad, (int)p.ncb, GW,
+                       (int)(a.B * p.nchunk));
+  else
+    hipLaunchKernelGGL((lr_reduce_kernel<E>), dim3((unsigned)grid), dim3(256), 0, s, dzp, dUp,
+                       (E *)a.dz, (E *)a.dU, N, a.R, (int)p.rpad, (int)p.ncb, GW,
+                       (int)(a.B * p.nchunk));
   return hipGetLastError();
 }
 
