@@ -856,6 +856,70 @@ CEILING_MIXES = {
 }
 
 
+def lds_banks():
+    """How the LDS serves one wave's access for the address patterns behind
+    the kernels' LDS layouts (libdsc_ldsprobe.so, see csrc/lds_probe.hip):
+    clock units per instruction, and the ratio to the op's conflict-free
+    linear pattern.  Prints a markdown table (profiles/lds_banks.md)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "dynamic_short_causal_amd", "libdsc_ldsprobe.so"))
+    lib.dsc_lds_probe.argtypes = [ctypes.POINTER(ctypes.c_uint), ctypes.c_int,
+                                  ctypes.POINTER(ctypes.c_double)]
+    ops = ["16-byte read", "8-byte read", "8-byte transposing read", "16-byte write",
+           "8-byte write", "2-byte write"]
+    size = [16, 8, 8, 16, 8, 2]
+    j_, q_ = (lambda i: i & 15), (lambda i: i >> 4)
+    paired = lambda vi: (2 * (vi >> 2) + ((vi & 3) >> 1)) * 32 + (vi & 1) * 256
+    gen_swz = lambda j: (0x78 >> (2 * ((j >> 2) & 3))) & 3
+    pats = [
+        (0, "linear (lane i at 16 i)", lambda i: 16 * i),
+        (0, "stride 32", lambda i: 32 * i),
+        (0, "stride 64", lambda i: 64 * i),
+        (0, "stride 256", lambda i: 256 * i),
+        (0, "16 lanes per 256-byte row, rows 256 apart", lambda i: (i % 16) * 16 + (i // 16) * 256),
+        (0, "16 lanes per 256-byte row, rows 272 apart", lambda i: (i % 16) * 16 + (i // 16) * 272),
+        (0, "16 lanes per 256-byte row, rows 288 apart", lambda i: (i % 16) * 16 + (i // 16) * 288),
+        (0, "16 lanes per 256-byte row, rows 512 apart", lambda i: (i % 16) * 16 + (i // 16) * 512),
+        (0, "8 lanes per 128-byte row, rows 256 apart", lambda i: (i % 8) * 16 + (i // 8) * 256),
+        (0, "8 lanes per 128-byte row, rows 384 apart", lambda i: (i % 8) * 16 + (i // 8) * 384),
+        (0, "GEMM fragment, granule q ^ (j >> 2) (before)",
+         lambda i: j_(i) * 64 + 16 * (q_(i) ^ (j_(i) >> 2))),
+        (0, "GEMM fragment, granule q ^ perm(j >> 2) (kept)",
+         lambda i: j_(i) * 64 + 16 * (q_(i) ^ gen_swz(j_(i)))),
+        (0, "low-rank ring read, plain vector order (before)", lambda i: j_(i) * 528 + q_(i) * 32),
+        (0, "low-rank ring read, quarters paired 256 B apart (kept)",
+         lambda i: j_(i) * 528 + paired(q_(i))),
+        (1, "linear (lane i at 8 i)", lambda i: 8 * i),
+        (1, "stride 16", lambda i: 16 * i),
+        (1, "stride 32", lambda i: 32 * i),
+        (2, "linear (lane i at 8 i)", lambda i: 8 * i),
+        (2, "stride 32", lambda i: 32 * i),
+        (2, "low-rank backward ring read: row 4q + j/4 (pitch 288), quad j % 4",
+         lambda i: (4 * q_(i) + (j_(i) >> 2)) * 288 + 8 * (j_(i) & 3)),
+        (3, "linear (lane i at 16 i)", lambda i: 16 * i),
+        (3, "low-rank ring write, plain vector order (16 lanes per row, 528 apart)",
+         lambda i: (i // 16) * 528 + (i % 16) * 32),
+        (3, "low-rank ring write, paired order, first half of odd vectors swapped (kept)",
+         lambda i: (i // 16) * 528 + paired(i % 16) + 16 * ((i % 16) & 1)),
+        (4, "linear (lane i at 8 i)", lambda i: 8 * i),
+        (4, "stride 32", lambda i: 32 * i),
+        (5, "linear (lane i at 2 i)", lambda i: 2 * i),
+        (5, "stride 64", lambda i: 64 * i),
+    ]
+    base = {}
+    rows = ["| access | lane address pattern | clock units per instruction | x linear |",
+            "|---|---|---|---|"]
+    for op, name, f in pats:
+        offs = (ctypes.c_uint * 64)(*[f(i) for i in range(64)])
+        out = ctypes.c_double(0.0)
+        rc = lib.dsc_lds_probe(offs, op, ctypes.byref(out))
+        if rc != 0:
+            raise RuntimeError(f"dsc_lds_probe failed ({rc}) for {ops[op]} {name}")
+        base.setdefault(op, out.value)
+        rows.append(f"| {ops[op]} | {name} | {out.value:.2f} | {out.value / base[op]:.2f} |")
+    return "\n".join(rows)
+
+
 def stream_ceilings(torch, dev, reps=8):
     """Best HBM rate of a plain streaming kernel (libdsc_stream.so) for each
     read/write mix of the step's ops, at the step's tensor sizes (x: B*T*D
@@ -977,6 +1041,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lds-banks", action="store_true",
+                    help="print the LDS access-pattern costs behind the kernels' LDS layouts")
     ap.add_argument("--profile-ops", type=int, default=0,
                     help="run each op this many times (and a copy of known size), no timing")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -1033,6 +1099,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.lds_banks:
+        print(lds_banks(), flush=True)
+        return
     if args.other_configs:
         print(json.dumps({"other_configs": other_configs(dsc, di, torch)}), flush=True)
         return

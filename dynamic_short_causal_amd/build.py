@@ -102,6 +102,7 @@ def build(jobs=None):
     build_c_consumer()
     build_stream_ceiling()
     build_yardstick()
+    build_lds_probe()
     return LIB
 
 
@@ -139,6 +140,23 @@ def build_yardstick():
         raise RuntimeError(f"hipcc failed for yardstick.hip:\n{r.stderr}")
     os.replace(tmp, YARD_LIB)
     return YARD_LIB
+
+
+LDSPROBE_SRC = os.path.join(CSRC, "lds_probe.hip")
+LDSPROBE_LIB = os.path.join(PKG, "libdsc_ldsprobe.so")
+
+
+def build_lds_probe():
+    """libdsc_ldsprobe.so: the LDS access probe the benchmark's --lds-banks
+    mode runs (not part of libdsc.so)."""
+    tmp = LDSPROBE_LIB + ".tmp"
+    cmd = [HIPCC, *[f for f in FLAGS if not f.startswith("-Rpass")], "-shared", LDSPROBE_SRC,
+           "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for lds_probe.hip:\n{r.stderr}")
+    os.replace(tmp, LDSPROBE_LIB)
+    return LDSPROBE_LIB
 
 
 CONSUMER_SRC = os.path.join(PKG, "examples", "c_consumer.c")
