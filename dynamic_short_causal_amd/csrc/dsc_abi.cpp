@@ -226,8 +226,9 @@ static dsc_status lowrank_check(int64_t B, int64_t T, int64_t D, int W, int H, i
                                 dsc_dtype dtype, unsigned flags, int *V) {
   dsc_status st = check_common(B, T, D, W, H, dtype, flags, V);
   if (st != DSC_OK) return st;
-  if (*V % H)
-    return fail(DSC_ERR_UNSUPPORTED, "H=%d: low-rank needs H to divide %d", H, *V);
+  if (*V % H && H % *V)
+    return fail(DSC_ERR_UNSUPPORTED, "H=%d: low-rank needs H to divide %d or be a multiple of it",
+                H, *V);
   if (R < 1 || R > 64) return fail(DSC_ERR_UNSUPPORTED, "R=%d outside 1..64", R);
   return DSC_OK;
 }

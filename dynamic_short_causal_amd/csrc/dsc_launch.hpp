@@ -30,6 +30,14 @@ struct LrArgs {
   void *stream;
 };
 
+// Filters tied over hm whole channel vectors (H = hm * vector width): the
+// low-rank kernels then tile one group per vector and read U's column of
+// group c / H.  1 when a vector holds one or more groups.
+inline int lr_tie_multiple(const LrArgs &a) {
+  const int V = a.bf16 ? 8 : 4;
+  return a.H > V ? a.H / V : 1;
+}
+
 // Workgroup shape of the low-rank backward for per-channel bf16 filters without
 // activation (lr_bwd_cl_kernel): waves, 16-channel groups per wave, and the
 // workgroups resident on one CU.
@@ -90,14 +98,16 @@ inline LrBwdPlan lr_bwd_plan(int64_t B, int64_t T, int64_t D, int W, int H, int 
                              bool cl) {
   LrBwdPlan p{};
   p.V = bf16 ? 8 : 4;
-  p.gpv = p.V / H;
+  p.gpv = H >= p.V ? 1 : p.V / H;
   p.units = 1;  // channel vectors per lane (LrGeo::NU)
   p.cb = cl ? kLrClCB : (int64_t)4 /*waves*/ * 4 /*quarters*/ * p.units * p.V;
   p.ncb = (D + p.cb - 1) / p.cb;
   p.rpad = 16 * lr_rank_blocks(R);  // whole 16-row MFMA blocks of ranks
   p.tc = pick_chunk(B, T, p.ncb, (cl ? kLrClResident : 3) * 256);
   p.nchunk = (T + p.tc - 1) / p.tc;
-  const int64_t G = D / H;
+  // groups of a dU partial row: those of the kernels' tiling, one per vector
+  // when the filters are tied over several vectors
+  const int64_t G = D / (H > p.V ? p.V : H);
   p.dz_part = (size_t)p.ncb * (size_t)(B * T) * (size_t)p.rpad * 4;
   p.dU_part = (size_t)(B * p.nchunk) * (size_t)p.rpad * (size_t)(G * W) * 4;
   p.bytes = p.dz_part + p.dU_part;

@@ -130,15 +130,19 @@ __device__ __forceinline__ void ring_store(unsigned char *row, int vv, const flo
 }
 
 // Filter slot sigma = k*NG + m of lane quarter qq; m = u*GPV + gi names vector
-// u*4 + qq of the wave slice and group gi inside it.  Returns the U column,
-// or -1 when the channel lies beyond D.
+// u*4 + qq of the wave slice and group gi inside it.  Returns the column of
+// the slot's filter in a (., G*W) matrix, or -1 when the channel lies beyond
+// D.  With filters tied over more channels than a vector holds (H = hm * V,
+// GPV = 1) the kernels tile by vector: the vector's own column is that of its
+// group in a matrix of D/V groups (hm = 1: dU partials), U's column that of
+// group c / H (hm = H / V).
 template <typename E, int W, int GPV>
-__device__ __forceinline__ int slot_col(int cw, int qq, int k, int m, int D) {
+__device__ __forceinline__ int slot_col(int cw, int qq, int k, int m, int D, int hm = 1) {
   using Gm = LrGeo<E, W, GPV>;
   const int u = m / GPV, gi = m % GPV;
   const int c = cw + (u * 4 + qq) * Gm::V;
   if (c >= D) return -1;
-  return (c / Gm::H + gi) * W + k;
+  return ((c / Gm::H + gi) / hm) * W + k;
 }
 
 // A operands of the filter MFMAs: for tap k, part p, rank step ks, lane (qa, i)
@@ -146,7 +150,7 @@ __device__ __forceinline__ int slot_col(int cw, int qq, int k, int m, int D) {
 // the output goes to lane quarter qo as slot m = 4p + e of tap k.
 template <typename E, int W, int GPV, int RB>
 __device__ __forceinline__ void load_wA(
-    const E *__restrict__ U, int GW, int R, int cw, int D, int lane,
+    const E *__restrict__ U, int GW, int R, int cw, int D, int hm, int lane,
     typename WFrag<sizeof(E) == 2>::T (&a)[W][LrGeo<E, W, GPV, RB>::NP][LrGeo<E, W, GPV, RB>::KS]) {
   using Gm = LrGeo<E, W, GPV, RB>;
   const int qa = lane >> 4, i = lane & 15, qo = i >> 2, e = i & 3;
@@ -155,7 +159,7 @@ __device__ __forceinline__ void load_wA(
 #pragma unroll
     for (int p = 0; p < Gm::NP; ++p) {
       const int m = 4 * p + e;
-      const int col = m < Gm::NG ? slot_col<E, W, GPV>(cw, qo, k, m, D) : -1;
+      const int col = m < Gm::NG ? slot_col<E, W, GPV>(cw, qo, k, m, D, hm) : -1;
 #pragma unroll
       for (int ks = 0; ks < Gm::KS; ++ks) {
         if constexpr (Gm::BF) {
@@ -250,7 +254,7 @@ template <typename E, int W, int GPV, bool ACT, bool VL, int RB>
 __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
     const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U,
     const int32_t *__restrict__ pos, E *__restrict__ y, int T, int D, int R, int TC,
-    int nchunk, int ncb, float rho) {
+    int nchunk, int ncb, float rho, int hm) {
   using Gm = LrGeo<E, W, GPV, RB>;
   using Fg = LrFwdGeo<E, W, GPV>;
   constexpr int V = Gm::V, NU = Gm::NU, NP = Gm::NP, KS = Gm::KS;
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
   const int b = bid / nchunk;
   const int cw = cb * Gm::CB + wave * Gm::CW;
   const int t0 = chunk * TC, t1 = min(T, t0 + TC);
-  const int GW = (D / Gm::H) * W;
+  const int GW = (D / Gm::H / hm) * W;  // U's row: D / H groups of W taps
   const int64_t seq = (int64_t)b * T;
   // row-major role: vector vv of rows rr, rr + RPP, ...
   const int vv = tid % VPR, rr = tid / VPR;
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(kLrThreads) void lr_fwd_kernel(
   };
 
   typename WFrag<Gm::BF>::T aw[W][NP][KS];
-  load_wA<E, W, GPV, RB>(U, GW, R, cw, D, lane, aw);
+  load_wA<E, W, GPV, RB>(U, GW, R, cw, D, hm, lane, aw);
 
   // the 16 rows before the chunk (zero before the sequence)
 #pragma unroll
@@ -474,7 +478,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
     const E *__restrict__ x, const E *__restrict__ z, const E *__restrict__ U,
     const E *__restrict__ dy, const int32_t *__restrict__ pos, E *__restrict__ dx,
     float *__restrict__ dzp, float *__restrict__ dUp, int T, int D, int R, int TC, int nchunk,
-    int ncb, int64_t N, float rho, int act, int rb0, int do_dx) {
+    int ncb, int64_t N, float rho, int act, int rb0, int do_dx, int hm) {
   using Gm = LrGeo<E, W, GPV, RB>;
   using Bg = LrBwdGeo<E, W, GPV, RB>;
   constexpr bool BF = Gm::BF;
@@ -504,7 +508,8 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
   const int b = bid / nchunk;
   const int cw = cb * Gm::CB + wave * Gm::CW;
   const int t0 = chunk * TC, t1 = min(T, t0 + TC);
-  const int GW = (D / Gm::H) * W;
+  const int GWp = (D / Gm::H) * W;  // a dU partial row: one group per vector or finer
+  const int GW = GWp / hm;          // U's row: D / H groups of W taps
   const int64_t seq = (int64_t)b * T;
   E *dwt = reinterpret_cast<E *>(smem + Bg::o_dwt + wave * Bg::dwt_wave);
 
@@ -559,7 +564,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
   for (int i = tid; i < 32 * ZP / 4; i += kLrThreads) reinterpret_cast<uint32_t *>(zring)[i] = 0u;
 
   typename WFrag<BF>::T aw[W][NP][KS];
-  load_wA<E, W, GPV, RB>(U, GW, R, cw, D, lane, aw);
+  load_wA<E, W, GPV, RB>(U, GW, R, cw, D, hm, lane, aw);
   typename DzFrag<BF>::T adz[NDZ];
   {
     const int qa = lane >> 4, r = 16 * rb0 + (lane & 15);
@@ -571,13 +576,13 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
         for (int e2 = 0; e2 < 8; ++e2) {
           const int sg = 8 * s + e2;
           int col = -1;
-          if (sg < NS) col = slot_col<E, W, GPV>(cw, qa, sg / NG, sg % NG, D);
+          if (sg < NS) col = slot_col<E, W, GPV>(cw, qa, sg / NG, sg % NG, D, hm);
           const uint16_t bits = (col >= 0 && r < R) ? (uint16_t)U[(int64_t)r * GW + col] : 0;
           f[e2] = __builtin_bit_cast(__bf16, bits);
         }
         adz[s] = f;
       } else {
-        const int col = slot_col<E, W, GPV>(cw, qa, s / NG, s % NG, D);
+        const int col = slot_col<E, W, GPV>(cw, qa, s / NG, s % NG, D, hm);
         adz[s] = (col >= 0 && r < R) ? (float)U[(int64_t)r * GW + col] : 0.f;
       }
     }
@@ -894,7 +899,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
   flush(tiles);
   {
     const int qo = lane >> 4, n = lane & 15;
-    float *dst = dUp + (int64_t)(b * nchunk + chunk) * RP * GW;
+    float *dst = dUp + (int64_t)(b * nchunk + chunk) * RP * GWp;
 #pragma unroll
     for (int a = 0; a < NRB; ++a) {
       const int sg = 4 * a + qo;
@@ -903,7 +908,7 @@ __global__ __launch_bounds__(kLrThreads, (lr_bwd_min_waves<E, W, GPV, VL, RB>())
       for (int e = 0; e < 4; ++e) {
         const int col = slot_col<E, W, GPV>(cw, e, sg / NG, sg % NG, D);
         if (col < 0) continue;
-        dst[(int64_t)(16 * rb0 + n) * GW + col] = accU[a][e];
+        dst[(int64_t)(16 * rb0 + n) * GWp + col] = accU[a][e];
       }
     }
   }
@@ -915,7 +920,11 @@ __global__ __launch_bounds__(256) void lr_reduce_kernel(const float *__restrict_
                                                          const float *__restrict__ dUp,
                                                          E *__restrict__ dz, E *__restrict__ dU,
                                                          int64_t N, int R, int RP, int ncb,
-                                                         int64_t GW, int nparts) {
+                                                         int64_t GW, int nparts, int W, int hm) {
+  // dU is R x GW (GW = G*W); a partial row holds hm times as many groups when
+  // filters are tied over hm vectors (one group per vector in the kernels),
+  // and dU sums the hm adjacent groups of its own after the parts
+  const int64_t GWp = GW * hm;
   const int64_t nz = N * R, nu = (int64_t)R * GW;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nz + nu;
        idx += (int64_t)gridDim.x * blockDim.x) {
@@ -929,18 +938,24 @@ __global__ __launch_bounds__(256) void lr_reduce_kernel(const float *__restrict_
     } else {
       const int64_t o = idx - nz;
       const int64_t r = o / GW, col = o - r * GW;
-      src = dUp + r * GW + col; stride = (int64_t)RP * GW; cnt = nparts;
+      const int64_t g = col / W, k = col - g * W;
+      src = dUp + r * GWp + g * hm * W + k; stride = (int64_t)RP * GWp; cnt = nparts;
     }
     float acc = 0.f;
-    int c = 0;
-    for (; c + 8 <= cnt; c += 8) {
-      float v[8];
+    if (idx >= nz && hm > 1) {
+      for (int c = 0; c < cnt; ++c)
+        for (int i = 0; i < hm; ++i) acc += src[c * stride + i * W];
+    } else {
+      int c = 0;
+      for (; c + 8 <= cnt; c += 8) {
+        float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = src[(c + i) * stride];
+        for (int i = 0; i < 8; ++i) v[i] = src[(c + i) * stride];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc += v[i];
+        for (int i = 0; i < 8; ++i) acc += v[i];
+      }
+      for (; c < cnt; ++c) acc += src[c * stride];
     }
-    for (; c < cnt; ++c) acc += src[c * stride];
     if constexpr (sizeof(E) == 2) {
       if (idx < nz) dz[idx] = __builtin_bit_cast(uint16_t, (__bf16)acc);
       else dU[idx - nz] = __builtin_bit_cast(uint16_t, (__bf16)acc);
@@ -953,8 +968,8 @@ __global__ __launch_bounds__(256) void lr_reduce_kernel(const float *__restrict_
 
 // The same sums, four consecutive outputs per thread with 16-byte loads of
 // the partials (R and G*W multiples of 4, so that four consecutive outputs
-// share a token row of dz or a rank row of dU).  Same order of addition per
-// output, so the same bits.
+// share a token row of dz or a rank row of dU; filters tied over at most one
+// vector).  Same order of addition per output, so the same bits.
 template <typename E>
 __global__ __launch_bounds__(256) void lr_reduce4_kernel(const float *__restrict__ dzp,
                                                           const float *__restrict__ dUp,

@@ -25,7 +25,7 @@ static hipError_t launch_lr_fwd_mfma(const LrArgs &a) {
   hipLaunchKernelGGL((lr_fwd_kernel<E, W, GPV, ACT, VL, RB>), dim3((unsigned)nblocks),
                      dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
                      (const E *)a.U, a.pos, (E *)a.y, (int)a.T, (int)a.D, a.R, TC, nchunk, ncb,
-                     rho);
+                     rho, lr_tie_multiple(a));
   return hipGetLastError();
 }
 
@@ -86,7 +86,7 @@ static hipError_t launch_lr_bwd(const LrArgs &a) {
                          dim3(kLrThreads), smem, s, (const E *)a.x, (const E *)a.z,
                          (const E *)a.U, (const E *)a.dy, a.pos, (E *)a.dx, dzp, dUp,
                          (int)a.T, (int)a.D, a.R, p.tc, (int)p.nchunk, (int)p.ncb, N, rho,
-                         a.act ? 1 : 0, rb0, rb0 == 0 ? 1 : 0);
+                         a.act ? 1 : 0, rb0, rb0 == 0 ? 1 : 0, lr_tie_multiple(a));
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -101,8 +101,9 @@ static hipError_t launch_lr_reduce(const LrArgs &a, const LrBwdPlan &p, const fl
   hipStream_t s = (hipStream_t)a.stream;
   const int64_t N = a.B * a.T;
   const int64_t GW = (a.D / a.H) * a.W;
+  const int hm = lr_tie_multiple(a);
   // four outputs per thread where R and G*W allow it (16-byte partial loads)
-  const bool by4 = a.R % 4 == 0 && GW % 4 == 0;
+  const bool by4 = a.R % 4 == 0 && GW % 4 == 0 && hm == 1;
   const int64_t total = (N * a.R + (int64_t)a.R * GW) / (by4 ? 4 : 1);
   int64_t grid = (total + 255) / 256;
   if (grid > 4096) grid = 4096;
@@ -114,7 +115,7 @@ static hipError_t launch_lr_reduce(const LrArgs &a, const LrBwdPlan &p, const fl
   else
     hipLaunchKernelGGL((lr_reduce_kernel<E>), dim3((unsigned)grid), dim3(256), 0, s, dzp, dUp,
                        (E *)a.dz, (E *)a.dU, N, a.R, (int)p.rpad, (int)p.ncb, GW,
-                       (int)(a.B * p.nchunk));
+                       (int)(a.B * p.nchunk), a.W, hm);
   return hipGetLastError();
 }
 
@@ -132,7 +133,9 @@ static hipError_t lr_rb(const LrArgs &a) {
 template <typename E, int W, int RB, bool BWD, bool VL>
 static hipError_t lr_gpv(const LrArgs &a) {
   constexpr int V = Vw<E>::n;
-  switch (V / a.H) {
+  // groups per vector; filters tied over several vectors tile as one group
+  // per vector (lr_tie_multiple)
+  switch (a.H >= V ? 1 : V / a.H) {
     case 1: return lr_rb<E, W, 1, RB, BWD, VL>(a);
     case 2: return lr_rb<E, W, 2, RB, BWD, VL>(a);
     case 4: return lr_rb<E, W, 4, RB, BWD, VL>(a);

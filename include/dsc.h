@@ -50,7 +50,8 @@
  *                        dtype, or a tying factor H the kernels do not tile
  *                        (head-wise: H divides the vector width, or H is the
  *                        vector width times a power of two up to 64; low-rank:
- *                        H divides the vector width), or, for the low-rank
+ *                        H divides the vector width or is a multiple of it),
+ *                        or, for the low-rank
  *                        backward, 16 * D * (bytes per element) >= 2^31;
  *   DSC_ERR_WORKSPACE    workspace smaller than dsc_lowrank_bwd_workspace_bytes
  *                        (dsc_static_bwd_workspace_bytes for dsc_static_bwd),

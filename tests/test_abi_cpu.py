@@ -130,7 +130,7 @@ def test_empty_is_ok_and_queues_nothing(lib):
 
 
 def test_lowrank_checks(lib):
-    assert lr(lib, H=16, D=64) == UNSUP
+    assert lr(lib, H=12, D=48) == UNSUP                     # neither divides 8 nor a multiple of it
     assert lr(lib, R=0) == UNSUP
     assert lr(lib, R=65) == UNSUP
     assert lr(lib, U=0) == INVALID
@@ -142,7 +142,10 @@ def test_lowrank_checks(lib):
 def test_workspace_checks(lib):
     n = lib.dsc_lowrank_bwd_workspace_bytes(8, 2048, 6144, 4, 1, 16, 1)
     assert n > 0
-    assert lib.dsc_lowrank_bwd_workspace_bytes(8, 2048, 6144, 4, 16, 16, 1) == 0  # H=16
+    assert lib.dsc_lowrank_bwd_workspace_bytes(8, 2048, 6144, 4, 12, 16, 1) == 0  # H=12
+    # H=16 (two bf16 vectors per group): partials of one group per vector
+    assert (lib.dsc_lowrank_bwd_workspace_bytes(8, 2048, 6144, 4, 16, 16, 1)
+            == lib.dsc_lowrank_bwd_workspace_bytes(8, 2048, 6144, 4, 8, 16, 1))
     assert lib.dsc_lowrank_bwd_workspace_bytes(8, 2048, 6144, 9, 1, 16, 1) == 0
     assert lrb(lib, wsb=lib.dsc_lowrank_bwd_workspace_bytes(1, 8, 64, 4, 1, 16, 1) - 1) == WS
     assert lrb(lib, ws=0) == WS
@@ -209,7 +212,7 @@ def test_decode_checks(lib):
     assert b"overlaps" in lib.dsc_last_error()
     assert hdec(lib, y=A + 2 * BIG + 16) == INVALID          # y inside the state
     assert hdec(lib, B=-1) == INVALID
-    assert ldec(lib, H=16) == UNSUP                          # low-rank needs H | 8
+    assert ldec(lib, H=12, D=48) == UNSUP                    # low-rank: H | 8 or 8 | H
     assert ldec(lib, R=0) == UNSUP
     assert ldec(lib, U=0) == INVALID
     assert ldec(lib, st=A + BIG) == INVALID                  # state overlaps z

@@ -72,10 +72,10 @@ def test_headwise_tying(dsc, orc, dtype, H):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("H", [1, 2, 4, 8])
+@pytest.mark.parametrize("H", [1, 2, 4, 8, 16, 64])
 def test_lowrank_tying(dsc, orc, dtype, H):
-    if dtype == torch.float32 and H == 8:
-        pytest.skip("low-rank fp32 needs H | 4")
+    # H above the vector width (fp32: 8, 16, 64; bf16: 16, 64): one group spans
+    # several vectors
     roll(dsc, orc, True, 3, 9, 576, 4, H, dtype, True, False, 6100 + H)
 
 

@@ -48,6 +48,18 @@ def test_tying_f32(dsc, orc, H):
     run_case(dsc, orc, 2, 150, 512 + 64 * H, 4, H, 16, torch.float32, True, False, 7100 + H)
 
 
+# Filters tied over several channel vectors (H a multiple of the vector width:
+# 16, 24 and 64 in bf16, 8 and 32 in fp32): the kernels tile one group per
+# vector, read U's column of group c / H and fold the vector groups' dU
+# partials in the reduction.  D leaves a partial last channel block.
+@pytest.mark.parametrize("H,dt,act,R,D", [(16, "bf16", False, 16, 1072), (64, "bf16", True, 16, 1088),
+                                          (24, "bf16", False, 16, 1080), (16, "bf16", True, 40, 1072),
+                                          (8, "f32", False, 16, 552), (32, "f32", True, 7, 608)])
+def test_tying_wider_than_a_vector(dsc, orc, H, dt, act, R, D):
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    run_case(dsc, orc, 2, 150, D, 4, H, R, dtype, True, act, 7700 + H + R)
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 5, 6, 7, 8])
 def test_widths(dsc, orc, W):
     run_case(dsc, orc, 2, 67, 256, W, 1, 16, torch.bfloat16, True, False, 7200 + W)

@@ -88,9 +88,11 @@ def test_headwise_widths_silu(dsc, orc, W):
 
 
 @pytest.mark.parametrize("H,dtype", [(1, torch.bfloat16), (2, torch.bfloat16),
-                                     (8, torch.bfloat16), (1, torch.float32),
-                                     (2, torch.float32)],
-                         ids=["bf16-H1", "bf16-H2", "bf16-H8", "f32-H1", "f32-H2"])
+                                     (8, torch.bfloat16), (16, torch.bfloat16),
+                                     (1, torch.float32), (2, torch.float32),
+                                     (8, torch.float32)],
+                         ids=["bf16-H1", "bf16-H2", "bf16-H8", "bf16-H16", "f32-H1", "f32-H2",
+                              "f32-H8"])
 def test_lowrank_tying(dsc, orc, H, dtype):
     # 150 tokens: chunks and tiles end inside documents
     lr_case(dsc, orc, 2, 150, 512, 4, H, 16, dtype, True, False, 9200 + H,
