@@ -94,11 +94,11 @@ Span span(const char *name, const void *p, int64_t elems, int esize, bool out) {
   return Span{name, lo, lo + (uintptr_t)(elems * esize), out};
 }
 
+// H divides the vector width (whole groups in one vector), or a group spans
+// L = H / V whole vectors, at most one wave's 64 lanes
 bool headwise_h_ok(int H, int V) {
   if (V % H == 0) return true;
-  if (H % V) return false;
-  int L = H / V;
-  return L <= 64 && (L & (L - 1)) == 0;
+  return H % V == 0 && H / V <= 64;
 }
 
 dsc_status hip_status(hipError_t e) {
@@ -167,7 +167,7 @@ static dsc_status headwise_common(const void *x, const void *w, const void *dy,
   if (st != DSC_OK) return st;
   if (!headwise_h_ok(H, V))
     return fail(DSC_ERR_UNSUPPORTED,
-                "H=%d: head-wise needs H | %d or H = %d * 2^m with 2^m <= 64", H, V, V);
+                "H=%d: head-wise needs H | %d or H = %d * m with m <= 64", H, V, V);
   const int es = dtype == DSC_BF16 ? 2 : 4;
   const int64_t n_act = B * T * D, n_w = B * T * (D / H) * W;
   const Span sp = span("pos", pos, varlen ? B * T : 0, 4, false);
@@ -366,7 +366,7 @@ static dsc_status decode_common(const void *x, const void *w, const void *z, con
   if (st != DSC_OK) return st;
   if (!lowrank && !headwise_h_ok(H, V))
     return fail(DSC_ERR_UNSUPPORTED,
-                "H=%d: head-wise needs H | %d or H = %d * 2^m with 2^m <= 64", H, V, V);
+                "H=%d: head-wise needs H | %d or H = %d * m with m <= 64", H, V, V);
   const int es = dtype == DSC_BF16 ? 2 : 4;
   const int64_t G = D / H;
   Span s[5] = {span("x", x, B * D, es, false),
@@ -423,7 +423,7 @@ static dsc_status static_check(int64_t B, int64_t T, int64_t D, int W, int H, ds
   if (st != DSC_OK) return st;
   if (!headwise_h_ok(H, V))
     return fail(DSC_ERR_UNSUPPORTED,
-                "H=%d: the static path needs H | %d or H = %d * 2^m with 2^m <= 64", H, V, V);
+                "H=%d: the static path needs H | %d or H = %d * m with m <= 64", H, V, V);
   return DSC_OK;
 }
 

@@ -175,4 +175,31 @@ __device__ __forceinline__ float silu_grad_f(float s) {
   return sg * (1.0f + s * (1.0f - sg));
 }
 
+// ---- filter-gradient sum over the lanes of one group ------------------------
+// A filter group of L >= 1 lanes occupies an aligned run of L consecutive
+// lanes (lane % L is the lane's place in its group; the wave holds 64 / L
+// whole groups, any lanes past them idle).  After the call the group's first
+// lane holds the sum of a[j] over the group.  L a power of two: xor butterfly,
+// every lane of the group ends with the sum.  Otherwise a halving tree inside
+// the group: in round s (1, 2, 4, ...) a lane adds the value s lanes up if
+// that lane is still in its group, which leaves the first lane with the sum
+// of all L.
+template <int N>
+__device__ __forceinline__ void group_sum(float (&a)[N], int L, int lane_in_group) {
+  if ((L & (L - 1)) == 0) {
+    for (int m = 1; m < L; m <<= 1)
+#pragma unroll
+      for (int j = 0; j < N; ++j) a[j] += __shfl_xor(a[j], m);
+  } else {
+    for (int s = 1; s < L; s <<= 1) {
+      const bool in = lane_in_group + s < L;
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const float o = __shfl_down(a[j], s);
+        a[j] += in ? o : 0.f;
+      }
+    }
+  }
+}
+
 }  // namespace dsc

@@ -12,7 +12,9 @@
 // each x row is fetched once per chunk plus a (W-1)-row halo at the chunk
 // start.  Lanes of one filter group fetch the same filter row (merged by the
 // cache); when a group spans L > 1 lanes the filter gradient is summed across
-// those lanes with butterfly shuffles.  Every output element has one writer.
+// those lanes with shuffles, and the backward gives each wave 64 / L whole
+// groups (lanes past them idle when L is not a power of two).  Every output
+// element has one writer.
 //
 // Packed rows (VL): with document positions pos (B, T), the taps of token t
 // beyond pos[b,t] are zeroed before use, which removes every term that would
@@ -189,12 +191,7 @@ __device__ __forceinline__ void hw_bwd_token(
         for (int h = 0; h < HS; ++h) a = fmaf(ds[gi * HS + h], win[k][gi * HS + h], a);
         pw[gi][k] = (VL && k > 0 && k > p) ? 0.f : a;
       }
-    if constexpr (GPV == 1) {
-      // sum over the L lanes of the group (aligned, contiguous lanes)
-      for (int m = 1; m < L; m <<= 1)
-#pragma unroll
-        for (int k = 0; k < W; ++k) pw[0][k] += __shfl_xor(pw[0][k], m);
-    }
+    if constexpr (GPV == 1) group_sum<W>(pw[0], L, lane_in_group);
     if (GPV > 1 || lane_in_group == 0) {
       float flat[GPV * W];
 #pragma unroll
@@ -229,7 +226,7 @@ template <typename E, int W, int GPV, bool ACT, bool VL>
 __global__ __launch_bounds__(kThreads) void hw_bwd_kernel(
     const E *__restrict__ x, const E *__restrict__ w, const E *__restrict__ dy,
     const int32_t *__restrict__ pos, E *__restrict__ dx, E *__restrict__ dw, int T, int64_t D,
-    int64_t G, int H, int nvec, int nvb, int TC, int nchunk, float rho) {
+    int64_t G, int H, int nvec, int nvb, int TC, int nchunk, float rho, int U) {
   constexpr int V = Vw<E>::n;
   constexpr int UN = 4;
   int bid = blockIdx.x;
@@ -237,9 +234,12 @@ __global__ __launch_bounds__(kThreads) void hw_bwd_kernel(
   bid /= nvb;
   const int chunk = bid % nchunk;
   const int b = bid / nchunk;
-  const int v = vb * kThreads + threadIdx.x;
-  // Groups of L lanes are aligned and nvec is a multiple of L, so whole
+  // Each wave takes U = 64 / L * L consecutive vectors, whole groups of L
+  // lanes (U = 64 when L is a power of two); nvec is a multiple of L, so whole
   // groups retire together and the shuffles never mix active and idle lanes.
+  const int lane = threadIdx.x & 63;
+  if (lane >= U) return;
+  const int v = (vb * (kThreads / 64) + (int)(threadIdx.x >> 6)) * U + lane;
   if (v >= nvec) return;
 
   const int t0 = chunk * TC;
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void hw_bwd_kernel(
   const int64_t c0 = (int64_t)v * V;
   const int g0 = (v * V) / H;
   const int L = (GPV == 1) ? H / V : 1;
-  const int lane_in_group = (GPV == 1) ? (v % L) : 0;
+  const int lane_in_group = (GPV == 1) ? (lane % L) : 0;
   const int64_t base = (int64_t)b * T * D + c0;
   const E *xp = x + base;
   const E *dyp = dy + base;
@@ -325,22 +325,27 @@ template <typename E, int W, int GPV, bool ACT, bool VL>
 static hipError_t launch_hw(const HwArgs &a) {
   constexpr int V = Vw<E>::n;
   const int nvec = (int)(a.D / V);
-  const int nvb = (nvec + kThreads - 1) / kThreads;
   const int TC = pick_chunk((int)a.T);
   const int nchunk = (int)((a.T + TC - 1) / TC);
-  const int64_t nblocks = (int64_t)a.B * nchunk * nvb;
   const int64_t G = a.D / a.H;
   const float rho = a.residual ? 1.f : 0.f;
   hipStream_t s = (hipStream_t)a.stream;
   if (!a.bwd) {
+    const int nvb = (nvec + kThreads - 1) / kThreads;
+    const int64_t nblocks = (int64_t)a.B * nchunk * nvb;
     hipLaunchKernelGGL((hw_fwd_kernel<E, W, GPV, ACT, VL>), dim3((unsigned)nblocks),
                        dim3(kThreads), 0, s, (const E *)a.x, (const E *)a.w, a.pos, (E *)a.y,
                        (int)a.T, a.D, G, a.H, nvec, nvb, TC, nchunk, rho);
   } else {
+    const int L = GPV == 1 ? a.H / V : 1;  // lanes per filter group
+    const int U = 64 / L * L;              // lanes of a wave in whole groups
+    const int per = U * (kThreads / 64);   // vectors per workgroup
+    const int nvb = (nvec + per - 1) / per;
+    const int64_t nblocks = (int64_t)a.B * nchunk * nvb;
     hipLaunchKernelGGL((hw_bwd_kernel<E, W, GPV, ACT, VL>), dim3((unsigned)nblocks),
                        dim3(kThreads), 0, s, (const E *)a.x, (const E *)a.w, (const E *)a.dy,
                        a.pos, (E *)a.dx, (E *)a.dw, (int)a.T, a.D, G, a.H, nvec, nvb, TC,
-                       nchunk, rho);
+                       nchunk, rho, U);
   }
   return hipGetLastError();
 }

@@ -169,7 +169,7 @@ template <typename E, int W, int GPV, bool ACT>
 __global__ __launch_bounds__(kStBwdThreads) void st_bwd_kernel(
     const E *__restrict__ x, const E *__restrict__ w, const E *__restrict__ dy,
     E *__restrict__ dx, float *__restrict__ part, int T, int64_t D, int H, int nvec,
-    int nvb, int TC, int ncg, float rho) {
+    int nvb, int TC, int ncg, float rho, int U) {
   constexpr int V = Vw<E>::n, NT = GPV * W;
   constexpr int UN = 4;
   __shared__ float red[kStWaves][NT][64];
@@ -180,8 +180,10 @@ __global__ __launch_bounds__(kStBwdThreads) void st_bwd_kernel(
   const int b = bid / ncg;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int v = vb * 64 + lane;
-  const bool active = v < nvec;  // lanes past D only join the barrier
+  // the workgroup's waves share U = 64 / L * L vectors, whole groups of L
+  // lanes; lanes past U or past D only join the barrier
+  const int v = vb * U + lane;
+  const bool active = lane < U && v < nvec;
   const int t0 = min(T, (cg * kStWaves + wave) * TC);
   const int t1 = min(T, t0 + TC);
   const int64_t c0 = (int64_t)(active ? v : 0) * V;
@@ -241,13 +243,9 @@ __global__ __launch_bounds__(kStBwdThreads) void st_bwd_kernel(
       st_bwd_token<E, W, GPV, ACT>(dxp, D, t, t0, t1, T, rho, taps, win, acc, dwa, xr, dyr);
     }
   }
-  if constexpr (GPV == 1) {
-    // sum over the L lanes of a group: aligned runs of L lanes inside the wave
-    // (64 % L == 0), all active or all idle since nvec % L == 0
-    for (int m = 1; m < L; m <<= 1)
-#pragma unroll
-      for (int k = 0; k < W; ++k) dwa[k] += __shfl_xor(dwa[k], m);
-  }
+  // sum over the L lanes of a group: aligned runs of L lanes inside the wave,
+  // all active or all idle since nvec % L == 0
+  if constexpr (GPV == 1) group_sum<W>(dwa, L, lane % L);
 #pragma unroll
   for (int j = 0; j < NT; ++j) red[wave][j][lane] = dwa[j];
   __syncthreads();
@@ -309,12 +307,14 @@ static hipError_t launch_st(const StArgs &a) {
     return hipGetLastError();
   }
   if (a.B > 0 && a.T > 0) {
-    const int nvb = (nvec + 63) / 64;
+    const int L = GPV == 1 ? a.H / V : 1;  // lanes per filter group
+    const int U = 64 / L * L;              // vectors per workgroup, whole groups
+    const int nvb = (nvec + U - 1) / U;
     const int64_t nblocks = a.B * p.ncg * nvb;
     hipLaunchKernelGGL((st_bwd_kernel<E, W, GPV, ACT>), dim3((unsigned)nblocks),
                        dim3(kStBwdThreads), 0, s, (const E *)a.x, (const E *)a.w,
                        (const E *)a.dy, (E *)a.dx, (float *)a.ws, (int)a.T, a.D, a.H, nvec,
-                       nvb, p.tc, p.ncg, rho);
+                       nvb, p.tc, p.ncg, rho, U);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

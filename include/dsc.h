@@ -49,7 +49,7 @@
  *   DSC_ERR_UNSUPPORTED  W outside 1..8, R outside 1..64, an unknown flag or
  *                        dtype, or a tying factor H the kernels do not tile
  *                        (head-wise: H divides the vector width, or H is the
- *                        vector width times a power of two up to 64; low-rank:
+ *                        vector width times 1 .. 64; low-rank:
  *                        H divides the vector width or is a multiple of it),
  *                        or, for the low-rank
  *                        backward, 16 * D * (bytes per element) >= 2^31;

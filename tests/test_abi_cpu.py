@@ -101,7 +101,8 @@ INVALID, UNSUP, WS = 1, 2, 3
     (dict(dt=7), UNSUP), (dict(fl=4), UNSUP), (dict(B=-1), INVALID), (dict(T=-2), INVALID),
     (dict(D=0), INVALID), (dict(W=0), UNSUP), (dict(W=9), UNSUP), (dict(H=0), INVALID),
     (dict(D=60, H=7), INVALID), (dict(D=36, H=1), INVALID), (dict(D=36, H=1, dt=0), OK := 0),
-    (dict(H=3, D=48), UNSUP), (dict(H=24, D=48), UNSUP), (dict(H=8 * 128, D=8192), UNSUP),
+    (dict(H=3, D=48), UNSUP), (dict(H=12, D=48), UNSUP), (dict(H=8 * 128, D=8192), UNSUP),
+    (dict(H=8 * 65, D=8 * 65), UNSUP), (dict(H=6, D=48, dt=0), UNSUP),
     (dict(x=0), INVALID), (dict(y=0), INVALID), (dict(w=A + BIG + 2), INVALID),
     (dict(y=A + 8), INVALID), (dict(y=A + 64 * 8 * 2 - 16), INVALID),
     (dict(B=1 << 31), INVALID), (dict(B=1 << 20, T=1 << 10, D=512), INVALID),

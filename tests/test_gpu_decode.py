@@ -71,6 +71,12 @@ def test_headwise_tying(dsc, orc, dtype, H):
     roll(dsc, orc, False, 3, 9, 576, 4, H, dtype, True, False, 6000 + H)
 
 
+@pytest.mark.parametrize("H,dtype", [(24, torch.bfloat16), (72, torch.bfloat16),
+                                     (12, torch.float32)])
+def test_headwise_groups_of_non_power_of_two_vectors(dsc, orc, H, dtype):
+    roll(dsc, orc, False, 3, 9, 576, 4, H, dtype, True, True, 6100 + H)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("H", [1, 2, 4, 8, 16, 64])
 def test_lowrank_tying(dsc, orc, dtype, H):

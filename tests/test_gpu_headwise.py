@@ -55,6 +55,18 @@ def test_tying_factors(dsc, orc, dtype, H):
     run_case(dsc, orc, 2, 150, 2112, 4, H, dtype, True, False, 2000 + H)
 
 
+@pytest.mark.parametrize("H,dtype,act,W,D", [
+    (24, torch.bfloat16, False, 4, 2160), (48, torch.bfloat16, True, 3, 2160),
+    (40, torch.bfloat16, False, 7, 2000), (8 * 33, torch.bfloat16, True, 4, 2376),
+    (12, torch.float32, False, 4, 1200), (20, torch.float32, True, 5, 1000),
+    (4 * 63, torch.float32, False, 2, 1008)])
+def test_groups_of_non_power_of_two_lanes(dsc, orc, H, dtype, act, W, D):
+    """A group spans L = H / V lanes with L not a power of two (3, 6, 5, 33, 3,
+    5, 63): the backward gives each wave 64 // L whole groups; D leaves a
+    ragged last workgroup."""
+    run_case(dsc, orc, 2, 150, D, W, H, dtype, True, act, 2500 + H)
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 5, 6, 7, 8])
 def test_widths(dsc, orc, W):
     run_case(dsc, orc, 2, 131, 512, W, 16, torch.bfloat16, True, False, 3000 + W)

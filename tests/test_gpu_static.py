@@ -41,6 +41,15 @@ def test_tying_factors(dsc, orc, dtype, H):
     run_case(dsc, orc, 2, 600, 2112, 4, H, dtype, True, False, 8000 + H)
 
 
+@pytest.mark.parametrize("H,dtype,act,D", [
+    (24, torch.bfloat16, False, 2160), (8 * 33, torch.bfloat16, True, 2376),
+    (12, torch.float32, True, 1200), (4 * 63, torch.float32, False, 1008)])
+def test_groups_of_non_power_of_two_lanes(dsc, orc, H, dtype, act, D):
+    """L = H / V lanes per group, not a power of two: each workgroup takes
+    64 // L whole groups of lanes; D leaves a ragged last workgroup."""
+    run_case(dsc, orc, 2, 600, D, 4, H, dtype, True, act, 8500 + H)
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 5, 6, 7, 8])
 def test_widths(dsc, orc, W):
     run_case(dsc, orc, 2, 131, 512, W, 16, torch.bfloat16, True, False, 8100 + W)

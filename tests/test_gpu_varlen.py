@@ -81,6 +81,13 @@ def test_headwise_tying(dsc, orc, dtype, H):
     hw_case(dsc, orc, 2, 300, 1024, 4, H, dtype, True, False, 9000 + H, packing(2, 300, 1, 6))
 
 
+@pytest.mark.parametrize("H,dtype", [(24, torch.bfloat16), (8 * 33, torch.bfloat16),
+                                     (12, torch.float32)])
+def test_headwise_groups_of_non_power_of_two_lanes(dsc, orc, H, dtype):
+    # 1056 channels: 132 bf16 vectors (44 groups of 3, or 4 of 33), 264 fp32 (88 of 3)
+    hw_case(dsc, orc, 2, 300, 1056, 4, H, dtype, True, True, 9050 + H, packing(2, 300, 1, 6))
+
+
 @pytest.mark.parametrize("W", [2, 3, 5, 8])
 def test_headwise_widths_silu(dsc, orc, W):
     hw_case(dsc, orc, 2, 150, 512, W, 8, torch.bfloat16, True, True, 9100 + W,
