@@ -73,6 +73,17 @@ def test_widths(dsc, orc, W):
     run_case(dsc, orc, 1, 70, 256, W, 2, torch.float32, False, True, 3100 + W)
 
 
+@pytest.mark.parametrize("T", [8, 9, 10, 31, 33, 34, 41, 42])
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_chunk_boundaries(dsc, orc, T, W):
+    """Lengths around the kernels' token chunks (4 per forward wave, 8 per
+    backward wave, 32 per backward workgroup): a last chunk of 1 or 2 tokens,
+    shorter than the W-1 tokens the previous chunk's dx needs from it, and
+    chunks that open a new workgroup."""
+    run_case(dsc, orc, 2, T, 1024, W, 16, torch.bfloat16, True, W == 3, 7000 + 10 * T + W)
+    run_case(dsc, orc, 1, T, 512, W, 4, torch.float32, False, W == 2, 7100 + 10 * T + W)
+
+
 @pytest.mark.parametrize("residual,act", [(False, False), (True, False), (False, True),
                                           (True, True)])
 def test_epilogues(dsc, orc, residual, act):
