@@ -978,6 +978,52 @@ def stream_ceilings(torch, dev, reps=8):
     return out
 
 
+def access_order(torch, dev, reps=10):
+    """The head-wise forward's bytes (x and a quarter-size filter tensor read,
+    y written) moved by the plain probe of libdsc_stream.so in three
+    geometries: long per-lane strips (workgroups resident all at once),
+    short per-wave chunks swept in address order, and whole rows per
+    workgroup.  Two tensor sets alternate; median of `reps` launches."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "dynamic_short_causal_amd", "libdsc_stream.so"))
+    lib.dsc_stream_order.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 6 + [ctypes.c_void_p]
+    B, T, D = WORKLOAD["B"], WORKLOAD["T"], WORKLOAD["D"]
+    ncol = D * 2 // 16
+    n = B * T * ncol
+    sets = [(torch.ones(n * 16, dtype=torch.uint8, device=dev),
+             torch.ones(n * 4, dtype=torch.uint8, device=dev),
+             torch.empty(n * 16, dtype=torch.uint8, device=dev)) for _ in range(2)]
+    nbytes = n * 16 * 2 + n * 4
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    cases = [("long strips, 64 tokens per lane", 0, 64, 1),
+             ("short chunks, 4 tokens x 8 waves", 1, 4, 8),
+             ("whole rows, 1 per workgroup", 2, 1, 1),
+             ("whole rows, 4 per workgroup", 2, 4, 1),
+             ("whole rows, 16 per workgroup", 2, 16, 1),
+             ("whole rows, 64 per workgroup", 2, 64, 1)]
+    out = {}
+    for name, mode, ln, nw in cases:
+        def call(i):
+            x, w, y = sets[i % 2]
+            r = lib.dsc_stream_order(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                                     ctypes.c_void_p(y.data_ptr()), B, T, ncol, mode, ln, nw, sp)
+            assert r == 0, r
+        for i in range(2):
+            call(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            call(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        out[name] = {"us": round(ms * 1e3, 1), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    return {"bytes": nbytes, "config": f"B={B} T={T} D={D} bf16, filter tensor D/4 per token",
+            "timing": f"median of {reps} launches, two tensor sets alternating", "cases": out}
+
+
 def decode_bench(dsc, di, torch, dev, iters=200):
     """One-token steps at serving batches, for head-wise H=16 and low-rank R=16
     H=1 at D=6144, W=4, bf16, residual.  Two timings of `iters` steps in a row:
@@ -1066,6 +1112,8 @@ def main():
                     help="time the linear-RNN backward on the matrix-core kernel and on the "
                          "vector-ALU kernel of libdsc_yard.so; with --profile-ops, run each "
                          "that many times untimed (counter runs)")
+    ap.add_argument("--access-order", action="store_true",
+                    help="time the head-wise forward's bytes in three access orders and exit")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the streaming ceilings of the step's read/write mixes")
     ap.add_argument("--summarize-gen-profiles", metavar="DIR",
@@ -1107,6 +1155,9 @@ def main():
         return
     if args.ceilings:
         print(json.dumps({"stream_ceilings": stream_ceilings(torch, dev)}), flush=True)
+        return
+    if args.access_order:
+        print(json.dumps({"access_order": access_order(torch, dev)}), flush=True)
         return
     if args.tied8_backward:
         r = tied8_backward(dsc, di, torch, profile_calls=args.profile_ops)
