@@ -9,10 +9,11 @@
 // dynamic kernels against (gist.science summary, Efficiente
 // Trainingsimplementatie, bullet Prestaties).  The backward is the derivative.
 //
-// Forward mapping: one lane owns one 16-byte channel vector and walks a chunk
-// of tokens with the causal window in registers, as in the head-wise kernel,
-// but its filter taps are loaded once and kept in registers, so the kernel
-// streams only x in and y out.
+// Forward mapping: one lane owns one 16-byte channel vector with the causal
+// window in registers, in the head-wise forward's layouts (short chunks in
+// address order for W <= 4, long strips above), but its filter taps are
+// loaded once and kept in registers, so the kernel streams only x in and y
+// out.
 //
 // Backward mapping: a workgroup of kStWaves waves owns 64 channel vectors;
 // wave i walks chunk kStWaves * cg + i of them.  dx is formed as in the
@@ -91,6 +92,88 @@ __global__ __launch_bounds__(kStFwdThreads) void st_fwd_kernel(
         }
         st16nt(yp + (int64_t)(t + u) * D, pack<E>(o));
       }
+    }
+  }
+}
+
+// Forward for W <= 4 in the head-wise forward's short-chunk order: a wave
+// takes 4 consecutive tokens of one 64-vector column, loaded at once; the 8
+// waves of a workgroup take consecutive chunks of that column; workgroups run
+// column-fastest.  The x rows before a chunk come from the previous wave
+// through LDS (the first wave of a workgroup reads them from memory).
+constexpr int kStTallTW = 4, kStTallNW = 8;
+template <typename E, int W, int GPV, bool ACT>
+__global__ __launch_bounds__(64 * kStTallNW) void st_fwd_tall_kernel(
+    const E *__restrict__ x, const E *__restrict__ w, E *__restrict__ y, int T, int64_t D,
+    int H, int nvec, int ncol, int nchunk, float rho) {
+  constexpr int V = Vw<E>::n, HS = V / GPV, NT = GPV * W;
+  constexpr int TW = kStTallTW, NW = kStTallNW, HR = W > 1 ? W - 1 : 1;
+  static_assert(TW >= W - 1, "the window lies in the previous chunk");
+  __shared__ uint4 xs[NW][HR][64];  // the last W-1 x rows of each wave's chunk
+  int bid = blockIdx.x;
+  const int col = bid % ncol;
+  bid /= ncol;
+  const int cgs = (nchunk + NW - 1) / NW;
+  const int cg = bid % cgs;
+  const int b = bid / cgs;
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int chunk = cg * NW + wave;
+  const int v = col * 64 + lane;
+  const bool active = chunk < nchunk && v < nvec;
+  const int t0 = chunk * TW;
+  const int t1 = min(T, t0 + TW);
+  const int64_t c0 = (int64_t)v * V;
+  const E *xp = x + (int64_t)b * T * D + c0;
+  E *yp = y + (int64_t)b * T * D + c0;
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+  uint4 xr[TW], hr[HR];
+  float taps[NT];
+  if (active) {
+#pragma unroll
+    for (int u = 0; u < TW; ++u)
+      if (t0 + u < t1) xr[u] = ld16nt(xp + (int64_t)(t0 + u) * D);
+    unpack_row<E, NT>(ld_row<E, NT>(w + (c0 / H) * W), taps);
+    if (wave == 0) {
+#pragma unroll
+      for (int k = 1; k < W; ++k) {
+        hr[k - 1] = z4;
+        if (t0 - k >= 0) hr[k - 1] = ld16nt(xp + (int64_t)(t0 - k) * D);
+      }
+    }
+    if (W > 1 && t1 - t0 == TW) {  // later chunks of this workgroup exist only then
+#pragma unroll
+      for (int i = 0; i < HR; ++i) xs[wave][i][lane] = xr[TW - HR + i];
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  if (wave > 0) {
+#pragma unroll
+    for (int k = 1; k < W; ++k) hr[k - 1] = xs[wave - 1][HR - k][lane];
+  }
+  // win[k] = x_{t-k} while token t is processed
+  float win[W][V];
+#pragma unroll
+  for (int k = 1; k < W; ++k) unpack<E>(hr[k - 1], win[k - 1]);
+#pragma unroll
+  for (int u = 0; u < TW; ++u) {
+    if (t0 + u < t1) {
+#pragma unroll
+      for (int k = W - 1; k > 0; --k)
+#pragma unroll
+        for (int i = 0; i < V; ++i) win[k][i] = win[k - 1][i];
+      unpack<E>(xr[u], win[0]);
+      float o[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int gi = i / HS;
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < W; ++k) s = fmaf(taps[gi * W + k], win[k][i], s);
+        if constexpr (ACT) s = silu_f(s);
+        o[i] = fmaf(rho, win[0][i], s);
+      }
+      st16nt(yp + (int64_t)(t0 + u) * D, pack<E>(o));
     }
   }
 }
@@ -297,6 +380,15 @@ static hipError_t launch_st(const StArgs &a) {
   const StPlan p = st_plan(a.B, a.T, a.D, a.W, a.H);
   if (!a.bwd) {
     if (a.B == 0 || a.T == 0) return hipSuccess;
+    if constexpr (W <= 4) {
+      const int nchunk = (int)((a.T + kStTallTW - 1) / kStTallTW);
+      const int ncol = (nvec + 63) / 64;
+      const int64_t nblocks = a.B * ((nchunk + kStTallNW - 1) / kStTallNW) * ncol;
+      hipLaunchKernelGGL((st_fwd_tall_kernel<E, W, GPV, ACT>), dim3((unsigned)nblocks),
+                         dim3(64 * kStTallNW), 0, s, (const E *)a.x, (const E *)a.w, (E *)a.y,
+                         (int)a.T, a.D, a.H, nvec, ncol, nchunk, rho);
+      return hipGetLastError();
+    }
     const int tc = a.T < kStFwdChunk ? (int)a.T : kStFwdChunk;
     const int nchunk = (int)((a.T + tc - 1) / tc);
     const int nvb = (nvec + kStFwdThreads - 1) / kStFwdThreads;
