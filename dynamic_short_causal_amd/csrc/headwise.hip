@@ -109,12 +109,14 @@ __global__ __launch_bounds__((64 * HwTile<E, W, GPV>::FNW)) void hw_fwd_kernel(
 
   uint4 xr[TW], hr[HR];
   RowBits<E, GPV * W> wr[TW];
+  int pr[VL ? TW : 1];  // document positions (packed rows), fetched with the rows
   if (active) {
 #pragma unroll
     for (int u = 0; u < TW; ++u)
       if (t0 + u < t1) {
         xr[u] = ld16nt(xp + (int64_t)(t0 + u) * D);
         wr[u] = ld_row<E, GPV * W, true>(wp + (int64_t)(t0 + u) * wstride);
+        if constexpr (VL) pr[u] = pos[(int64_t)b * T + t0 + u];
       }
     // x_{t0-k} from before the workgroup's first chunk (zero before the
     // sequence start); x_{t0-k} lies in the chunk d = ceil(k / TW) waves back
@@ -150,7 +152,7 @@ __global__ __launch_bounds__((64 * HwTile<E, W, GPV>::FNW)) void hw_fwd_kernel(
       unpack<E>(xr[u], win[0]);
       float taps[GPV * W];
       unpack_row<E, GPV * W>(wr[u], taps);
-      if constexpr (VL) mask_taps<W, GPV>(taps, pos[(int64_t)b * T + t0 + u]);
+      if constexpr (VL) mask_taps<W, GPV>(taps, pr[u]);
       float o[V];
 #pragma unroll
       for (int i = 0; i < V; ++i) {
@@ -345,6 +347,7 @@ __global__ __launch_bounds__((64 * HwTile<E, W, GPV>::BNW), (HwTile<E, W, GPV>::
   if constexpr (kLdsWin) {
     uint4 xr[TW], dyr[TW];
     RowBits<E, GPV * W> wr[TW];
+    int pr[VL ? TW : 1];  // document positions (packed rows), fetched with the rows
     if (active) {
 #pragma unroll
       for (int u = 0; u < TW; ++u)
@@ -352,6 +355,7 @@ __global__ __launch_bounds__((64 * HwTile<E, W, GPV>::BNW), (HwTile<E, W, GPV>::
           xr[u] = ld16nt(xp + (int64_t)(t0 + u) * D);
           dyr[u] = ld16nt(dyp + (int64_t)(t0 + u) * D);
           wr[u] = ld_row<E, GPV * W, true>(wp + (int64_t)(t0 + u) * wstride);
+          if constexpr (VL) pr[u] = pos[(int64_t)b * T + t0 + u];
         }
       if (W > 1 && t1 - t0 == TW) {  // later chunks of this workgroup exist only then
 #pragma unroll
@@ -367,7 +371,11 @@ __global__ __launch_bounds__((64 * HwTile<E, W, GPV>::BNW), (HwTile<E, W, GPV>::
       window(hl);
 #pragma unroll
       for (int u = 0; u < TW; ++u)
-        if (t0 + u < t1) token(t0 + u, xr[u], dyr[u], wr[u], VL ? pos[(int64_t)b * T + t0 + u] : 0);
+        if (t0 + u < t1) {
+          int p = 0;
+          if constexpr (VL) p = pr[u];
+          token(t0 + u, xr[u], dyr[u], wr[u], p);
+        }
     }
   } else {
     if (active) {
