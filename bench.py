@@ -60,7 +60,9 @@ KERNEL_SOURCES = {
                      "dynamic_short_causal_amd/csrc/dsc_device.hpp"],
     "headwise_bwd": ["dynamic_short_causal_amd/csrc/headwise.hip",
                      "dynamic_short_causal_amd/csrc/dsc_device.hpp"],
-    "lowrank_fwd": ["dynamic_short_causal_amd/csrc/lowrank_impl.hpp",
+    "lowrank_fwd": ["dynamic_short_causal_amd/csrc/lowrank_fwd_cl.hpp",
+                    "dynamic_short_causal_amd/csrc/lowrank_bwd_cl.hpp",
+                    "dynamic_short_causal_amd/csrc/lowrank_impl.hpp",
                     "dynamic_short_causal_amd/csrc/lowrank_launch.hpp",
                     "dynamic_short_causal_amd/csrc/dsc_device.hpp"],
     "lowrank_bwd": ["dynamic_short_causal_amd/csrc/lowrank_impl.hpp",
@@ -149,7 +151,7 @@ def cpu_baseline(target_s=12.0):
 OP_KERNELS = {  # op -> kernel names (rocprofv3) that one call launches
     "headwise_fwd": ["hw_fwd_kernel"],
     "headwise_bwd": ["hw_bwd_kernel"],
-    "lowrank_fwd": ["lr_fwd_kernel"],
+    "lowrank_fwd": ["lr_fwd_cl_kernel", "lr_fwd_kernel"],
     "lowrank_bwd": ["lr_bwd_cl_kernel", "lr_bwd_kernel", "lr_reduce4_kernel", "lr_reduce_kernel"],
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"  # the 512 MiB device copy of --profile-ops
