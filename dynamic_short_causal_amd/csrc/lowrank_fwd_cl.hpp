@@ -1,5 +1,5 @@
 // lowrank_fwd_cl.hpp -- low-rank forward for per-channel filters (H = 1,
-// bf16, R <= 16), one channel per lane.
+// bf16, plain rows, R <= 16), one channel per lane.
 //
 // Operation: the low-rank dynamic short convolution (gist.science summary
 // "Dynamische Korte Convoluties Verbeteren Transformers", Methodologie >
@@ -21,10 +21,6 @@
 // transposing LDS read (ds_read_b64_tr_b16: four token rows of one channel
 // into one lane).  y goes back through a 16-row LDS staging tile and is
 // stored in whole rows.
-//
-// Packed rows (VL): document positions of the step's tokens go through a
-// 32-entry LDS ring; tap k of a token beyond its position is dropped where
-// the lane holds that token's filter, right after the MFMA.
 #pragma once
 #include "lowrank_bwd_cl.hpp"
 
@@ -37,21 +33,18 @@ template <int W> struct LrFwdClGeo {
   static constexpr int o_x = 0;
   static constexpr int o_y = o_x + 32 * XP;
   static constexpr int o_z = o_y + 16 * XP;
-  static constexpr int o_pos = o_z + 32 * ZP;  // 32 document positions (VL)
-  static constexpr int bytes = o_pos + 32 * 4;
+  static constexpr int bytes = o_z + 32 * ZP;
 };
 
-template <int W, bool ACT, bool VL, int PF>
+template <int W, bool ACT, int PF>
 __global__ __launch_bounds__(kClThreads) void lr_fwd_cl_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ z, const bf16 *__restrict__ U,
-    const int32_t *__restrict__ pos, bf16 *__restrict__ y, int T, int D, int R, int TC,
-    int nchunk, int ncb, float rho) {
+    bf16 *__restrict__ y, int T, int D, int R, int TC, int nchunk, int ncb, float rho) {
   using Gc = LrFwdClGeo<W>;
   constexpr int XP = Gc::XP, ZP = Gc::ZP, NHQ = Gc::NHQ, NG = kClNG, VPR = kClVPR;
   static_assert(kClThreads == 16 * VPR, "one x vector of a 16-row slab per thread");
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char *xring = smem + Gc::o_x, *yst = smem + Gc::o_y, *zring = smem + Gc::o_z;
-  int *pring = reinterpret_cast<int *>(smem + Gc::o_pos);
 
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, n = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -113,13 +106,8 @@ __global__ __launch_bounds__(kClThreads) void lr_fwd_cl_kernel(
   // (compile-time after unrolling the step loop by PF)
   uint4 xn[PF];
   bf16 zn[PF];
-  int pn[PF];
   auto issue = [&](int st, int sl) {
     const int t = t0 + 16 * st;
-    if constexpr (VL) {
-      const brsrc rp = mk_rsrc(pos + seq + t, (int64_t)(min(T, t + 16) - t) * 4);
-      pn[sl] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, tid < 16 ? (uint32_t)tid * 4 : kOOB, 0, 0);
-    }
     const brsrc rz = slab(z, t, T, R);
     zn[sl] = (bf16)__builtin_amdgcn_raw_buffer_load_b16(rz, zoff, 0, 0);
     const brsrc rx = slab(x, t, T, D);
@@ -129,7 +117,6 @@ __global__ __launch_bounds__(kClThreads) void lr_fwd_cl_kernel(
     const int t = t0 + 16 * st;
     *reinterpret_cast<uint4 *>(xring + ((t + cr) & 31) * XP + cv * 16) = xn[sl];
     if (z_on) reinterpret_cast<bf16 *>(zring + ((t + zr_tok) & 31) * ZP)[zr_rank] = zn[sl];
-    if (VL && tid < 16) pring[(t + tid) & 31] = pn[sl];
   };
   // y of step st from the staging tile, in whole rows (rows past t1 dropped)
   auto flush = [&](int st) {
@@ -148,11 +135,6 @@ __global__ __launch_bounds__(kClThreads) void lr_fwd_cl_kernel(
     __syncthreads();  // (1) ring rows of this step written; staging of the last step read
     // A operand: row n = token t+n, ranks 4q..4q+3
     const s16x4 az = *reinterpret_cast<const s16x4 *>(zring + ((t + n) & 31) * ZP + 8 * q);
-    int pe[4];  // document positions of the lane's four tokens (VL)
-    if constexpr (VL) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pe[e] = pring[(t + 4 * q + e) & 31];
-    }
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
       // xw[4h + e] = x of this lane's channel at token t + 4q - 4*NHQ + 4h + e
@@ -169,11 +151,7 @@ __global__ __launch_bounds__(kClThreads) void lr_fwd_cl_kernel(
       for (int k = 0; k < W; ++k) {
         const f32x4 wk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(az, bu[u][k], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // tap k of a token before its document's start is dropped (VL)
-          const float wv = (VL && k > 0 && k > pe[e]) ? 0.f : wk[e];
-          o[e] = k == 0 ? wv * xw[X0 + e] : fmaf(wv, xw[X0 + e - k], o[e]);
-        }
+        for (int e = 0; e < 4; ++e) o[e] = k == 0 ? wk[e] * xw[X0 + e] : fmaf(wk[e], xw[X0 + e - k], o[e]);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

@@ -30,27 +30,27 @@ static hipError_t launch_lr_fwd_mfma(const LrArgs &a) {
   return hipGetLastError();
 }
 
-// per-channel bf16 filters, at most 16 ranks: one channel per lane
-// (lowrank_fwd_cl.hpp), loads two 16-token steps ahead
+// per-channel bf16 filters on plain rows, at most 16 ranks: one channel per
+// lane (lowrank_fwd_cl.hpp), loads two 16-token steps ahead
 constexpr int kLrFwdClPrefetch = 2;
-template <int W, bool ACT, bool VL>
+template <int W, bool ACT>
 static hipError_t launch_lr_fwd_cl(const LrArgs &a) {
   const int ncb = (int)((a.D + kClCB - 1) / kClCB);
   const int TC = pick_chunk(a.B, a.T, ncb, (int64_t)kLrClResident * 256);
   const int nchunk = (int)((a.T + TC - 1) / TC);
   const int64_t nblocks = a.B * nchunk * (int64_t)ncb;
   if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((lr_fwd_cl_kernel<W, ACT, VL, kLrFwdClPrefetch>), dim3((unsigned)nblocks),
+  hipLaunchKernelGGL((lr_fwd_cl_kernel<W, ACT, kLrFwdClPrefetch>), dim3((unsigned)nblocks),
                      dim3(kClThreads), LrFwdClGeo<W>::bytes, (hipStream_t)a.stream,
-                     (const bf16 *)a.x, (const bf16 *)a.z, (const bf16 *)a.U, a.pos, (bf16 *)a.y,
+                     (const bf16 *)a.x, (const bf16 *)a.z, (const bf16 *)a.U, (bf16 *)a.y,
                      (int)a.T, (int)a.D, a.R, TC, nchunk, ncb, a.residual ? 1.f : 0.f);
   return hipGetLastError();
 }
 
 template <typename E, int W, int GPV, bool ACT, bool VL, int RB>
 static hipError_t launch_lr_fwd(const LrArgs &a) {
-  if constexpr (std::is_same_v<E, bf16> && GPV == 8 && RB == 1) {
-    if (a.H == 1 && a.R <= 16) return launch_lr_fwd_cl<W, ACT, VL>(a);
+  if constexpr (std::is_same_v<E, bf16> && GPV == 8 && RB == 1 && !VL) {
+    if (a.H == 1 && a.R <= 16) return launch_lr_fwd_cl<W, ACT>(a);
   }
   // bf16 filters tied over 8 channels (one group per vector): vector ALUs
   if constexpr (std::is_same_v<E, bf16> && GPV == 1 && RB == 1 && W <= 4) {
