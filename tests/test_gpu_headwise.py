@@ -50,8 +50,8 @@ def test_tiny_f32_width_one_and_static(dsc, orc):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("H", [1, 2, 4, 8, 16, 64])
 def test_tying_factors(dsc, orc, dtype, H):
-    # 2 sequences, 150 tokens (three 64-token chunks, ragged), 2112 channels
-    # (a full and a ragged 256-lane block)
+    # 2 sequences, 150 tokens (ragged against the 4- and 8-token chunks and the
+    # 32-token backward workgroups), 2112 channels (a ragged last column)
     run_case(dsc, orc, 2, 150, 2112, 4, H, dtype, True, False, 2000 + H)
 
 
