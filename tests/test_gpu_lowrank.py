@@ -94,6 +94,15 @@ def test_many_ranks_short_sequences(dsc, orc, B, T):
     run_case(dsc, orc, B, T, 64, 4, 2, 33, torch.float32, True, False, 7595 + T)
 
 
+@pytest.mark.parametrize("B,T,D,W,act", [(4, 1041, 1536, 4, False), (2, 1041, 1536, 8, True),
+                                         (3, 129, 640, 2, True), (2, 527, 1000, 3, False)])
+def test_per_channel_chunks(dsc, orc, B, T, D, W, act):
+    """Per-channel bf16 filters (one channel per lane in both directions)
+    over lengths whose token chunks and 16-token steps end ragged, every
+    element checked."""
+    run_case(dsc, orc, B, T, D, W, 1, 16, torch.bfloat16, True, act, 7950 + T + W)
+
+
 @pytest.mark.parametrize("residual,act", [(False, False), (True, False), (False, True),
                                           (True, True)])
 def test_epilogues(dsc, orc, residual, act):
